@@ -1,0 +1,254 @@
+"""Pins of the oracle's tensor codec, accounting, rounding and metrics.
+
+Exact tile accounting from the paper's Table 5 (tests/golden), the model
+card's bpp and relative-L2 formulas on hand-computed tensors, container
+rounding against torch's casts, the decoded lattice against an independent
+quantisation of the same input, the least-squares row refit, rate targeting
+and rate-distortion behaviour.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthgen
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_table5_tile_accounting_exact():
+    gold = json.load(open(os.path.join(GOLD, "table5_tile_metadata.json")))
+    R, Cc = gold["rows"], gold["cols"]
+    for e in gold["entries"]:
+        V = oracle.default_vectors_per_tile(e["target_bpp"])
+        assert V == e["tile_vectors"] == max(32, e["tile_symbols"] // 9)
+        T = oracle.num_tiles(R, Cc, V)
+        assert T == e["tiles"]
+        assert oracle.default_prob_bits(e["target_bpp"]) == e["b"]
+        # metadata bytes: stored bytes with an empty payload and no tables minus the rest
+        zero = np.zeros(17, np.uint32)
+        with_tiles = oracle.stored_bytes(R, T, 0, zero)
+        no_tiles = oracle.stored_bytes(R, 0, 0, zero)
+        assert with_tiles - no_tiles + 4 == e["metadata_bytes"] == 132 * T + 4
+        # metadata share implies a total stored size near the target rate
+        total = e["metadata_bytes"] / (e["metadata_pct"] / 100.0)
+        assert abs(8 * total / (R * Cc) - e["target_bpp"]) / e["target_bpp"] < 0.04
+
+
+def test_stored_bytes_layout():
+    alpha = np.array([2] + [3] * 8 + [0] * 8, np.uint32)
+    # header 32 + c-table 4 + 16 x (4 + 2) + 8 x 3 x 2 + rows x 4 + 132 T + 4 + 2 words
+    expect = 32 + 4 + 16 * 6 + 8 * 3 * 2 + 10 * 4 + 132 * 3 + 4 + 2 * 100
+    assert oracle.stored_bytes(10, 3, 100, alpha) == expect
+    assert oracle.stored_bytes(10, 3, 100, alpha, "fp8") == expect + 40
+
+
+def test_bpp_and_rel_l2_formulas():
+    # model card: bpp = 8 * sum(bytes) / sum(numel); ratio = bpp / 16
+    assert oracle.bpp([100, 28], [200, 56]) == pytest.approx(4.0, abs=0)
+    # weight error = sqrt(sum ||Wq - W||^2) / sqrt(sum ||W||^2)
+    W = np.array([3.0, 4.0, 0.0, 0.0], np.float32)
+    Wq = np.array([3.0, 4.0, 1.0, 2.0], np.float32)
+    assert oracle.rel_l2(Wq, W) == pytest.approx(np.sqrt(5.0) / 5.0, rel=1e-15)
+    assert oracle.rel_l2(W, W) == 0.0
+
+
+def _f32_samples():
+    rng = np.random.default_rng(0)
+    a = [rng.normal(0, s, 200_000).astype(np.float32) for s in (1e-3, 0.05, 1.0, 30.0, 300.0)]
+    # exact ties for bf16 and fp8 rounding, signed zeros, boundaries
+    ties = (np.arange(-3000, 3000, dtype=np.int64).astype(np.float32) * np.float32(0.0625))
+    special = np.array([0.0, -0.0, 448.0, -448.0, 449.0, 464.0, 465.0, 1e6, -1e6,
+                        2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -6, 127.5, -128.5,
+                        126.5, 0.5, -0.5, 1.5, 2.5], np.float32)
+    bits = rng.integers(0, 2 ** 31, 100_000, dtype=np.int64).astype(np.uint32).view(np.float32)
+    bits = bits[np.isfinite(bits)]
+    return np.concatenate(a + [ties, special, bits])
+
+
+def test_bf16_rounding_matches_torch():
+    y = _f32_samples()
+    mine = oracle.f32_to_bf16(y)
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_fp8_rounding_matches_torch_after_clamp():
+    y = _f32_samples()
+    mine = oracle.f32_to_fp8(y)
+    clamped = np.clip(y, -448.0, 448.0)
+    ref = torch.from_numpy(clamped).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    # every code decodes to the value torch gives it
+    codes = np.arange(256, dtype=np.uint8)
+    tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = oracle.fp8_value(c)
+        assert (np.isnan(v) and np.isnan(tv[c])) or v == tv[c]
+
+
+def test_int8_rounding_matches_torch():
+    y = _f32_samples()
+    mine = oracle.f32_to_int8(y)
+    ref = torch.clamp(torch.round(torch.from_numpy(y).double()), -128, 127).to(torch.int8).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def _small(seed=0, rows=64, cols=256, outliers=0.0):
+    return synthgen.student_t_weights(rows, cols, seed, outlier_frac=outliers).numpy()
+
+
+def test_decoded_lattice_matches_independent_quantisation():
+    W = _small(1, 96, 512)
+    ct = oracle.encode(W, 4.0, V=100, b=11)
+    lat, st = oracle.decode(ct, "lattice2x")
+    assert np.all(st == 0)
+    # independent: u = W / rms(row), v = u / s, nearest E8 point (pinned above)
+    n = np.sqrt((W.astype(np.float64) ** 2).mean(axis=1))
+    v = (W.astype(np.float64) / n[:, None]) / np.float64(np.float32(ct.s))
+    x, _ = oracle.e8_nearest(v.reshape(-1, 8))
+    assert np.array_equal(lat.reshape(-1, 8), (2 * x).astype(np.int32))
+
+
+def test_decoded_values_follow_row_scales():
+    W = _small(2, 40, 256)
+    ct = oracle.encode(W, 5.0, V=64)
+    lat, _ = oracle.decode(ct, "lattice2x")
+    y, _ = oracle.decode(ct, "f32")
+    g = np.float32(ct.s) * ct.row_scales.astype(np.float32)       # fp32 products
+    expect = (lat.astype(np.float32) * np.float32(0.5)) * g[:, None]
+    assert np.array_equal(y, expect.astype(np.float32))
+    bf, _ = oracle.decode(ct, "bf16")
+    ref = torch.from_numpy(expect.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(bf, ref.view(np.uint16))
+
+
+def test_row_refit_is_least_squares():
+    W = _small(3, 50, 256)
+    ct = oracle.encode(W, 4.0, V=64)
+    lat, _ = oracle.decode(ct, "lattice2x")
+    X = lat.astype(np.float64) / 2.0 * np.float64(np.float32(ct.s))
+    for r in range(W.shape[0]):
+        num = (W[r].astype(np.float64) * X[r]).sum()
+        den = (X[r] ** 2).sum()
+        assert ct.row_scales[r] == np.float32(num / den)
+    # the fitted scale does at least as well as the row RMS it started from
+    n = np.sqrt((W.astype(np.float64) ** 2).mean(axis=1))
+    fit = ((W - ct.row_scales[:, None] * X) ** 2).sum()
+    base = ((W - n[:, None] * X) ** 2).sum()
+    assert fit <= base
+
+
+def test_rate_targeting_and_rate_distortion():
+    W = synthgen.student_t_weights(1536, 1024, 77, bf16=True).numpy()
+    errs = {}
+    for tgt in (2.0, 4.0, 6.0, 8.0):
+        ct = oracle.encode(W, tgt)
+        assert abs(ct.bpp / tgt - 1.0) < 0.03, (tgt, ct.bpp)   # pages: max 2.13%
+        bf, st = oracle.decode(ct, "bf16")
+        assert np.all(st == 0)
+        errs[tgt] = oracle.rel_l2(oracle.bf16_to_f32(bf), W)
+    # about 6 dB per bit: 4 more bits cut the error ~16x (pages: 7.19% -> 0.51%)
+    assert 10.0 < errs[4.0] / errs[8.0] < 20.0
+    assert errs[2.0] > errs[4.0] > errs[6.0] > errs[8.0]
+
+
+def test_estimate_decreases_with_scale():
+    W = _small(4, 128, 512)
+    ests = [oracle.estimate_bpp(W, s, 11, 455) for s in (0.05, 0.1, 0.2, 0.4, 0.8)]
+    assert all(a > b for a, b in zip(ests, ests[1:]))
+
+
+def test_alphabet_escalation_raises_b():
+    # 0.1% outliers x20 at 8 bpp need more than 12 bits of probability precision
+    W = synthgen.workload("w3840_8bpp")[0].weights().numpy()
+    ct = oracle.encode(W, 8.0)
+    assert ct.b > 12
+    assert ct.alphabet[1:].max() <= 1 << ct.b
+    _, st = oracle.decode(ct, "bf16")
+    assert np.all(st == 0)
+
+
+def test_coarsening_at_max_precision():
+    # a lone outlier keeps |u| = sqrt(cols) = 64 after row normalisation; at the
+    # fine scales a 16 bpp target asks for, its field needs more than 2^15 symbols
+    W = _small(6, 512, 4096)
+    W[0, 0] = 1e4
+    ct = oracle.encode(W, 13.0)
+    assert ct.b == 15 and ct.alphabet[1:].max() <= 1 << 15
+    # the searched scale was coarsened, so the stored rate falls short of the target
+    assert ct.bpp < 0.97 * 13.0
+    _, st = oracle.decode(ct, "bf16")
+    assert np.all(st == 0)
+
+
+def test_partial_tile_range_and_ragged_tail():
+    W = _small(7, 33, 64)           # 264 vectors, V = 50 -> last tile of 14 vectors
+    ct = oracle.encode(W, 4.0, V=50)
+    assert ct.T == 6
+    full, st = oracle.decode(ct, "bf16")
+    part, st2 = oracle.decode(ct, "bf16", 2, 5)
+    assert np.all(st2[2:5] == 0) and np.all(st2[:2] == -1) and np.all(st2[5:] == -1)
+    flat_full, flat_part = full.reshape(-1), part.reshape(-1)
+    lo, hi = 2 * 50 * 8, 5 * 50 * 8
+    assert np.array_equal(flat_full[lo:hi], flat_part[lo:hi])
+    assert np.all(flat_part[:lo] == 0) and np.all(flat_part[hi:] == 0)
+
+
+def test_empty_tensor():
+    W = np.zeros((0, 64), np.float32)
+    ct = oracle.encode(W, 4.0)
+    assert ct.T == 0 and ct.nwords == 0
+    out, st = oracle.decode(ct, "bf16")
+    assert out.shape == (0, 64)
+
+
+def test_zero_rows_decode_to_zero():
+    W = _small(8, 16, 128)
+    W[3] = 0.0
+    ct = oracle.encode(W, 4.0, V=32)
+    bf, st = oracle.decode(ct, "bf16")
+    assert np.all(bf[3] == 0)
+
+
+def test_route_precast_fp8_and_int8():
+    W = _small(9, 20, 128)
+    Wq, q = oracle.route_precast(W, "fp8")
+    amax = np.abs(W).max(axis=1)
+    assert np.array_equal(q, (amax / np.float32(448.0)).astype(np.float32))
+    y = (W / q[:, None]).astype(np.float32)
+    ref = torch.from_numpy(np.clip(y, -448, 448)).to(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(Wq, ref)
+    Wi, qi = oracle.route_precast(W, "int8")
+    yi = (W / qi[:, None]).astype(np.float32)
+    assert np.array_equal(Wi, np.clip(np.rint(yi), -127, 127))
+    assert np.abs(Wi).max() == 127
+
+
+def test_fp8_route_round_trip_codes():
+    W = _small(10, 64, 256)
+    ct = oracle.encode(W, 5.0, route="fp8")
+    codes, st = oracle.decode(ct, "fp8")
+    assert np.all(st == 0)
+    Wq, _ = oracle.route_precast(W, "fp8")
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    e = oracle.rel_l2(vals, Wq)
+    assert e < 0.1
+
+
+def test_tensor_fault_injection_flags_tiles():
+    W = _small(11, 64, 256)
+    ct = oracle.encode(W, 4.0, V=64)
+    assert ct.T == 32
+    bad = dict(payload=ct.payload.copy(), states=ct.states.copy())
+    t1 = 5
+    bad["payload"][ct.offsets[t1] + 3] ^= 0x0100
+    bad["states"][32 * 9 + 4] ^= 0x40
+    import dataclasses
+    ct2 = dataclasses.replace(ct, payload=bad["payload"], states=bad["states"])
+    _, st = oracle.decode(ct2, "bf16")
+    assert st[t1] != 0 and st[9] != 0
+    assert np.all(np.delete(st, [t1, 9]) == 0)
