@@ -1,0 +1,44 @@
+"""Build the gfx950 HIP library in-tree with hipcc.
+
+Produces dit_weight_compression_amd/libentropack_mi355x.so from csrc/*.hip.
+Always recompiles (the caller decides when to build).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_NAME = "libentropack_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = [os.path.join(HERE, "csrc", "ep_decode.hip")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",           # y = x * g must round once, never fuse
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = [HIPCC] + FLAGS + list(extra_flags or []) + SOURCES + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra_flags=sys.argv[1:])

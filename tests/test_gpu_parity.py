@@ -1,0 +1,199 @@
+"""GPU parity: the HIP decoder against the CPU oracle, through the C ABI.
+
+Inputs are seeded synthetic tensors compressed by the oracle's encoder; the
+GPU decodes the same arrays.  Lattice coordinates, FP8 and INT8 codes and BF16
+bit patterns must match bit for bit (BF16 follows the oracle's fp32 operation
+order y = fp32(x * fp32(s * r_row)), so no tolerance is needed).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthgen
+
+pytestmark = pytest.mark.gpu
+
+ep = pytest.importorskip("dit_weight_compression_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.lib()
+
+
+def _gpu_out_numpy(t: torch.Tensor, kind: str) -> np.ndarray:
+    if kind == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if kind == "fp8":
+        return t.view(torch.uint8).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def _check_parity(ct, kinds=("bf16", "lattice2x"), label=""):
+    p = ep.PackedTensor.from_arrays(ct)
+    for kind in kinds:
+        ref, rst = oracle.decode(ct, kind)
+        out, st = ep.decode_tensor(p, kind, with_status=True)
+        torch.cuda.synchronize()
+        got = _gpu_out_numpy(out, kind)
+        assert np.all(st.cpu().numpy()[: ct.T] == 0), f"{label} {kind}: tile status"
+        assert np.all(rst == 0)
+        if not np.array_equal(got, ref):
+            bad = np.argwhere(got != ref)
+            raise AssertionError(f"{label} {kind}: {len(bad)} mismatches, first at {bad[:5].tolist()}")
+
+
+def test_library_exports_and_version():
+    L = ep.lib()
+    for name in ep.EXPORTS:
+        assert hasattr(L, name)
+    assert L.ep_abi_version() == 1
+
+
+@pytest.mark.parametrize("V", [512, 455])
+def test_w256x512_4bpp_bit_exact(V):
+    spec = synthgen.workload("w256x512_4bpp_fp32" if V == 512 else "w256x512_4bpp_fp32_s4096")[0]
+    W = spec.weights().numpy()
+    ct = oracle.encode(W, spec.target_bpp, V=spec.vectors_per_tile, b=spec.prob_bits)
+    assert ct.b == 12 and ct.V == V
+    _check_parity(ct, label=f"V={V}")
+
+
+@pytest.mark.parametrize("b", list(range(9, 16)))
+def test_every_precision(b):
+    # scale picked so the alphabets fit 2^b; ragged shapes, V not a multiple of 32
+    rng = np.random.default_rng(b)
+    rows, cols = int(rng.integers(3, 70)), 8 * int(rng.integers(1, 90))
+    W = synthgen.student_t_weights(rows, cols, 100 + b).numpy()
+    s = {9: 0.5, 10: 0.25, 11: 0.1, 12: 0.05, 13: 0.02, 14: 0.01, 15: 0.004}[b]
+    ct = oracle.encode_fixed_scale(W, s, V=int(rng.integers(32, 200)), b=b)
+    _check_parity(ct, label=f"b={b} {rows}x{cols} V={ct.V}")
+
+
+def test_routes_fp8_and_int8_codes():
+    W = synthgen.student_t_weights(96, 1024, 42).numpy()
+    ct8 = oracle.encode(W, 5.0, route="fp8")
+    _check_parity(ct8, kinds=("fp8", "lattice2x", "bf16"), label="fp8 route")
+    cti = oracle.encode(W, 8.0, route="int8")
+    _check_parity(cti, kinds=("int8", "lattice2x"), label="int8 route 8bpp")
+    cti2 = oracle.encode(W, 2.0, route="int8")
+    _check_parity(cti2, kinds=("int8",), label="int8 route 2bpp")
+
+
+def test_int8_and_fp8_saturation_paths():
+    # decoding a direct-route tensor into INT8 / FP8 exercises clamping and subnormals
+    W = (synthgen.student_t_weights(64, 512, 7).numpy() * 4000.0).astype(np.float32)
+    ct = oracle.encode(W, 6.0)
+    _check_parity(ct, kinds=("int8", "fp8"), label="saturation")
+    Ws = (synthgen.student_t_weights(64, 512, 8).numpy() * 1e-2).astype(np.float32)
+    cts = oracle.encode(Ws, 6.0)
+    _check_parity(cts, kinds=("fp8",), label="fp8 subnormals")
+
+
+def test_single_symbol_and_empty_coset_tables():
+    # all-zero rows quantise to the origin: coset 1 never occurs (its tables are
+    # empty) and every coordinate table holds one symbol (f = M, no renormalisation)
+    W = np.zeros((16, 256), np.float32)
+    ct = oracle.encode_fixed_scale(W, 1.0, V=40, b=11)
+    assert ct.alphabet[2] == 0 and ct.alphabet[1] == 1
+    _check_parity(ct, label="degenerate tables")
+
+
+def test_batch_mixed_tensors_one_call():
+    rng = np.random.default_rng(3)
+    cts, kinds = [], []
+    for i in range(7):
+        rows, cols = int(rng.integers(1, 200)), 8 * int(rng.integers(1, 300))
+        W = synthgen.student_t_weights(rows, cols, 500 + i).numpy()
+        tgt = float(rng.choice([2.0, 4.0, 8.0]))
+        route = ["direct", "fp8", "int8"][i % 3]
+        cts.append(oracle.encode(W, tgt, V=int(rng.integers(32, 500)), route=route))
+        kinds.append({"direct": "bf16", "fp8": "fp8", "int8": "int8"}[route])
+    # an empty tensor in the middle of the batch
+    cts.insert(3, oracle.encode(np.zeros((0, 64), np.float32), 4.0))
+    kinds.insert(3, "bf16")
+    packed = [ep.PackedTensor.from_arrays(c) for c in cts]
+    outs, sts = ep.decode_batch(packed, kinds, with_status=True)
+    torch.cuda.synchronize()
+    for i, (ct, kind) in enumerate(zip(cts, kinds)):
+        ref, _ = oracle.decode(ct, kind)
+        assert np.array_equal(_gpu_out_numpy(outs[i], kind), ref), f"tensor {i}"
+        assert np.all(sts[i].cpu().numpy()[: ct.T] == 0)
+
+
+def test_deterministic_repeat_and_workspace_reuse():
+    W = synthgen.student_t_weights(300, 768, 9).numpy()
+    ct = oracle.encode(W, 4.0, V=100)
+    p = ep.PackedTensor.from_arrays(ct)
+    ws = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda")
+    a, _ = ep.decode_tensor(p, "bf16", workspace=ws)
+    b, _ = ep.decode_tensor(p, "bf16", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_corrupt_streams_flagged_like_oracle():
+    W = synthgen.student_t_weights(64, 512, 11).numpy()
+    ct = oracle.encode(W, 4.0, V=64)
+    rng = np.random.default_rng(0)
+    pl = ct.payload.copy()
+    stt = ct.states.copy()
+    off = ct.offsets.copy()
+    bad_tiles = set()
+    for t in (1, 4, 9):
+        pl[ct.offsets[t] + int(rng.integers(0, ct.offsets[t + 1] - ct.offsets[t]))] ^= np.uint16(0x0210)
+        bad_tiles.add(t)
+    stt[32 * 6 + 17] ^= np.uint32(0x100)
+    bad_tiles.add(6)
+    off[12] += 1          # tile 11 one word longer, tile 12 one word shorter
+    bad_tiles.update({11, 12})
+    ct2 = dataclasses.replace(ct, payload=pl, states=stt, offsets=off)
+    _, rst = oracle.decode(ct2, "bf16")
+    p = ep.PackedTensor.from_arrays(ct2)
+    _, st = ep.decode_tensor(p, "bf16", with_status=True)
+    gst = st.cpu().numpy()[: ct.T]
+    assert set(np.nonzero(rst)[0].tolist()) == bad_tiles
+    assert np.array_equal(gst != 0, rst != 0)
+    # good tiles still decode exactly
+    ref, _ = oracle.decode(ct2, "bf16")
+    out, _ = ep.decode_tensor(p, "bf16")
+    got = _gpu_out_numpy(out, "bf16").reshape(-1)
+    for t in range(ct.T):
+        if t in bad_tiles:
+            continue
+        lo, hi = t * ct.V * 8, min((t + 1) * ct.V * 8, got.size)
+        assert np.array_equal(got[lo:hi], ref.reshape(-1)[lo:hi])
+
+
+def test_offsets_beyond_payload_are_contained():
+    W = synthgen.student_t_weights(32, 256, 12).numpy()
+    ct = oracle.encode(W, 4.0, V=32)
+    off = ct.offsets.copy()
+    off[-1] += 5000       # the last tile claims words that do not exist
+    ct2 = dataclasses.replace(ct, offsets=off)
+    p = ep.PackedTensor.from_arrays(ct2)
+    # the buffer really ends at the true payload end
+    p = dataclasses.replace(p, payload=p.payload[: int(ct.offsets[-1])].clone())
+    _, st = ep.decode_tensor(p, "bf16", with_status=True)
+    gst = st.cpu().numpy()[: ct.T]
+    assert gst[-1] != 0 and np.all(gst[:-1] == 0)
+
+
+def test_invalid_arguments_rejected():
+    W = synthgen.student_t_weights(8, 64, 1).numpy()
+    ct = oracle.encode(W, 4.0, V=32)
+    p = ep.PackedTensor.from_arrays(ct)
+    with pytest.raises(ep.EpError) as ei:
+        ep.decode_batch([dataclasses.replace(p, T=p.T + 1)], "bf16")
+    assert ei.value.status == ep.EP_ERR_INVALID_ARG
+    with pytest.raises(ep.EpError):
+        ep.decode_batch([dataclasses.replace(p, b=16)], "bf16")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ep.EpError) as ei:
+        ep.decode_batch([p], "bf16", workspace=small)
+    assert ei.value.status == ep.EP_ERR_WORKSPACE
