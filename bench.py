@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Decode-throughput benchmark of the fused EntroPack decoder on one MI355X.
+
+Workload (default): the DiT linear set -- 30 blocks x {QKV 3840->11520,
+out 3840->3840, FFN up 3840->10240, gate 3840->10240, down 10240->3840},
+150 tensors, 5,308,416,000 weights -- compressed at a 4 bpp target and decoded
+to BF16 by one ep_decode_batch call per step.  Weights are seeded synthetic
+Student-t tensors (nu = 5, per-row lognormal scales) rounded to BF16, drawn on
+the GPU and compressed by the host encoder before timing; the compressed
+streams and the outputs are resident in HBM when the timed region starts.
+
+A step is one complete ep_decode_batch call (schedule upload, decode-table
+build, fused decode kernel).  HIP events on the launch stream bracket every
+step and, separately, the decode kernel, whose average duration gives the
+roofline figure: algorithmic bytes = stored bytes (payload, tile metadata,
+tables, row scales, headers) + output bytes, against 8 TB/s.
+
+The CPU baseline times the CPU oracle decoding a bounded sample of the same
+containers on this host (one thread).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decoded Gweights/s + % HBM roofline, 4bpp→BF16, DiT linear set, 1 GPU"
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _load_cached(path):
+    import numpy as np
+
+    from dit_weight_compression_amd import encoder
+
+    z = np.load(path, allow_pickle=False)
+    meta = z["meta"]
+    rows, cols, V, T, b = (int(v) for v in meta[:5])
+    qs = z["route_scales"] if "route_scales" in z.files else None
+    return encoder.HostContainer(rows, cols, V, T, b, float(z["s"][0]), str(z["route"][0]),
+                                 float(z["est"][0]), int(meta[5]), z["row_scales"], qs, z["states"],
+                                 z["offsets"], z["payload"], z["freqs"], z["alphabet"],
+                                 z["minval"], z["freq_base"])
+
+
+def _save_cached(path, ct):
+    import numpy as np
+
+    extra = {} if ct.route_scales is None else {"route_scales": ct.route_scales}
+    tmp = path + ".tmp.npz"
+    np.savez(tmp, meta=np.array([ct.rows, ct.cols, ct.V, ct.T, ct.b, ct.stored_bytes], np.int64),
+             s=np.array([ct.s], np.float32), route=np.array([ct.route]), est=np.array([ct.est_bpp]),
+             row_scales=ct.row_scales, states=ct.states, offsets=ct.offsets, payload=ct.payload,
+             freqs=ct.freqs, alphabet=ct.alphabet, minval=ct.minval, freq_base=ct.freq_base, **extra)
+    os.replace(tmp, path)
+
+
+def build_inputs(specs, threads: int, device: str, cache_dir: str = ""):
+    """Draw, compress and upload every tensor (optionally via an on-disk container cache)."""
+    import torch
+
+    import dit_weight_compression_amd as ep
+    from dit_weight_compression_amd import encoder
+
+    packed, hosts = [], []
+    t0 = time.time()
+    if cache_dir:
+        os.makedirs(cache_dir, exist_ok=True)
+    for i, spec in enumerate(specs):
+        path = os.path.join(cache_dir, f"{spec.name}_{spec.seed}_{spec.target_bpp}_{spec.route}.npz") if cache_dir else ""
+        if path and os.path.exists(path):
+            ct = _load_cached(path)
+        else:
+            W = spec.weights(device=device).cpu().numpy()
+            ct = encoder.encode(W, spec.target_bpp, V=spec.vectors_per_tile or 0,
+                                b=spec.prob_bits or 0, route=spec.route, threads=threads)
+            del W
+            if path:
+                _save_cached(path, ct)
+        packed.append(ep.PackedTensor.from_arrays(ct, device=device, stored_bytes=ct.stored_bytes))
+        hosts.append(ct)
+        if (i + 1) % 5 == 0 or i + 1 == len(specs):
+            log(f"[bench] encoded {i + 1}/{len(specs)} tensors ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    return packed, hosts
+
+
+def cpu_baseline(hosts, dtype: str, budget_s: float):
+    """CPU oracle decoding whole tensors of the workload until the time budget is spent."""
+    import oracle
+
+    done_w, spent, names = 0, 0.0, 0
+    for ct in hosts:
+        t0 = time.perf_counter()
+        _, st = oracle.decode(ct, dtype)
+        spent += time.perf_counter() - t0
+        assert (st == 0).all()
+        done_w += ct.numel
+        names += 1
+        if spent >= budget_s:
+            break
+    return {"value": done_w / spent / 1e9, "unit": "Gweights/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {names} tensor(s) of the workload ({done_w} weights) decoded to "
+                      f"{dtype} by the single-threaded CPU oracle, {spent:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit_linear_set_30x5_4bpp_bf16")
+    ap.add_argument("--max-tensors", type=int, default=0, help="use only the first N tensors")
+    ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cache", default="", help="directory for compressed containers (reused if present)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this decoder benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported (tiles shard across GPUs "
+                                   "with no exchange; see the design notes)"}))
+        sys.exit(2)
+
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    ep.lib()
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    specs = synthgen.workload(args.workload)
+    if args.max_tensors:
+        specs = specs[: args.max_tensors]
+    dtypes = [s.out_dtype for s in specs]
+
+    packed, hosts = build_inputs(specs, args.threads, device, args.cache)
+    numel = sum(p.numel for p in packed)
+    stored = sum(p.stored_bytes for p in packed)
+    out_bytes = sum(p.numel * {"bf16": 2, "fp8": 1, "int8": 1}[d] for p, d in zip(packed, dtypes))
+    outs = ep.alloc_outputs(packed, dtypes, device)
+    ws = torch.empty(ep.workspace_size(packed), dtype=torch.uint8, device=device)
+    batch = ep.BatchArgs(packed, dtypes, outs, None, ws)
+    stream = torch.cuda.current_stream()
+    sp = ep.C.c_void_p(stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        batch.call(sp)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        plan = batch.prepare(sp)
+        ev[i][1].record(stream)
+        batch.launch(plan, sp)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    kern_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    ms = sum(step_ms) / len(step_ms)
+    kms = sum(kern_ms) / len(kern_ms)
+
+    # one more call with tile status to confirm every tile decoded cleanly
+    sts = [torch.full((max(p.T, 1),), -1, dtype=torch.int32, device=device) for p in packed]
+    ep.BatchArgs(packed, dtypes, outs, sts, ws).call(sp)
+    torch.cuda.synchronize()
+    tiles_ok = all(bool((s[: p.T] == 0).all()) for s, p in zip(sts, packed))
+
+    algo_bytes = stored + out_bytes
+    achieved = algo_bytes / (kms / 1e3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": numel / (ms / 1e3) / 1e9,
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "tensors": len(packed),
+            "weights": numel,
+            "target_bpp": specs[0].target_bpp if len(set(s.target_bpp for s in specs)) == 1 else "mixed",
+            "stored_bpp": 8.0 * stored / numel,
+            "out_dtype": dtypes[0] if len(set(dtypes)) == 1 else "mixed",
+            "tiles": sum(p.T for p in packed),
+            "kernel_ms": kms,
+            "kernel_ms_min": min(kern_ms),
+            "step_ms_min": min(step_ms),
+            "hbm_roofline_frac_of_step": algo_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "tiles_ok": tiles_ok,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+    }
+    log(f"[bench] {len(packed)} tensors, {numel / 1e9:.3f} G weights, {8 * stored / numel:.4f} bpp; "
+        f"step {ms:.3f} ms, kernel {kms:.3f} ms, wall {t_wall * 1e3 / args.steps:.3f} ms/step")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(hosts, dtypes[0], args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

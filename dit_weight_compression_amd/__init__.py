@@ -54,7 +54,7 @@ class EpTensorDesc(C.Structure):
 
 
 class EpBatchPlan(C.Structure):
-    _fields_ = [("opaque", C.c_uint64 * 16)]
+    _fields_ = [("opaque", C.c_uint64 * 64)]
 
 
 _lib = None
@@ -122,9 +122,7 @@ class PackedTensor:
     def numel(self) -> int:
         return self.rows * self.cols
 
-    @property
-    def nwords(self) -> int:
-        return int(self.payload.numel())
+    nwords: int = 0         # payload words (the device buffer is padded to a multiple of 8)
 
     @classmethod
     def from_arrays(cls, ct, device="cuda", stored_bytes: int = 0) -> "PackedTensor":
@@ -137,14 +135,18 @@ class PackedTensor:
                 a = np.zeros(1, np_dt)
             return torch.from_numpy(a.view(t_dt)).to(device)
 
-        nw = int(ct.offsets[-1]) if ct.T > 0 else 0
-        payload = up(np.asarray(ct.payload)[:nw], np.uint16, np.int16)
+        # words actually present (a corrupt final offset must not extend the buffer)
+        nw = min(int(ct.offsets[-1]), int(np.asarray(ct.payload).size)) if ct.T > 0 else 0
+        # the decoder reads whole 16-byte groups: pad the payload to a multiple of 8 words
+        padded = np.zeros(max((nw + 7) // 8 * 8, 8), np.uint16)
+        padded[:nw] = np.asarray(ct.payload)[:nw]
+        payload = up(padded, np.uint16, np.int16)
         return cls(int(ct.rows), int(ct.cols), int(ct.V), int(ct.T), int(ct.b), float(ct.s),
                    np.asarray(ct.alphabet, np.uint32).copy(), np.asarray(ct.minval, np.int32).copy(),
                    np.asarray(ct.freq_base, np.uint32).copy(),
                    up(ct.row_scales, np.float32, np.float32), up(ct.states, np.uint32, np.int32),
                    up(ct.offsets, np.uint32, np.int32), payload, up(ct.freqs, np.uint16, np.int16),
-                   stored_bytes)
+                   stored_bytes, nw)
 
     def desc(self) -> EpTensorDesc:
         d = EpTensorDesc()

@@ -24,34 +24,51 @@
 
 #include "entropack.h"
 
+// global (not flat) addressing for pointers read from the descriptors
+#define EP_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 namespace {
 
 constexpr uint32_t kL = 1u << 15;          // lower bound of the state interval
 constexpr int kTables = EP_NUM_TABLES;
 constexpr int kTilesPerWave = 2;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 16;
 constexpr int kBlock = 64 * kWavesPerBlock;
 constexpr int kTilesPerChunk = kTilesPerWave * kWavesPerBlock;
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Where a tensor's decode tables live while it is decoded: LDS with the
+// precision compiled in -- "wide" u16 slot maps for b = 9..11 and alphabets up
+// to 512, "narrow" u8 slot maps for b = 12 and alphabets up to 256 -- or the
+// workspace for everything else.
+enum Variant : uint32_t { kVarW9 = 0, kVarW10, kVarW11, kVarN12, kVarGlobal, kNumVariants };
 
 // Device-side view of one tensor (lives in the workspace).
 struct alignas(16) DevTensor {
   uint64_t nvec;             // rows * cols / 8
   uint32_t vpr;              // vectors per row = cols / 8
   uint32_t V, T, b;
+  uint32_t rows;
   float scale;
   uint32_t empty_mask;       // bit k: table k is empty
   int32_t dtype;
+  uint32_t variant;          // decode-table placement, see Variant
+  uint32_t kpar;             // bit c: parity of min_offset of fields z1..z7 in coset c
+  uint32_t tab_bytes;        // bytes of the table block copied to LDS (LDS variants)
   const float* row_scales;
   const uint32_t* states;
   const uint32_t* offsets;
   const uint16_t* payload;
   uint64_t payload_words;
+  uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
+  uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
   const uint16_t* freqs;
-  uint16_t* lut;             // [16][2^b] slot -> zero-based symbol (workspace)
-  uint32_t* symtab;          // per coordinate table: f | cum << 16 (workspace)
+  unsigned char* tab;        // workspace: decode tables, layout per variant
   void* out;
   int32_t* status;
-  uint32_t sym_base[kTables];
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
   uint32_t alphabet[kTables];
@@ -71,26 +88,60 @@ int fail(int code, const std::string& msg) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Decode-table layout.  For coordinate table t = 2*(field-1) + coset (16 of them):
+//   lut   [16][2^b]   slot -> zero-based symbol (u8 in the narrow LDS layout, u16 otherwise)
+//   sym   [16][S]     f | (cum + coset * 2^b) << 16   (S = 256 narrow, 512 wide, 2^b workspace);
+//                     in the LDS layouts bit 15 also holds the parity of the value of z1..z7
+//   val   [16][S]     float value the symbol stands for: z + c/2 for z1..z7, 2m + c/2 for m
+// Adding coset * 2^b to cum lets the decoder subtract the coset-offset slot directly.
+__host__ __device__ constexpr uint32_t lds_stride(bool wide) { return wide ? 512u : 256u; }
+__host__ __device__ constexpr size_t lds_lut_bytes(uint32_t b, bool wide) {
+  return (size_t(16) << b) * (wide ? 2 : 1);
+}
+__host__ __device__ constexpr size_t lds_table_bytes(uint32_t b, bool wide) {
+  return lds_lut_bytes(b, wide) + 2 * size_t(16) * lds_stride(wide) * 4;
+}
+__host__ __device__ constexpr size_t global_table_bytes(uint32_t b) {
+  return (size_t(16) << b) * 2 + 2 * (size_t(16) << b) * 4;
+}
+
 // ---------------------------------------------------------------- table build
 // One block per (coordinate table, tensor): cumulative frequencies by a block
-// scan, then the slot -> symbol table by a binary search per slot.
+// scan, then the slot -> symbol map by a binary search per slot.
 __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __restrict__ tens) {
   const DevTensor& T = tens[blockIdx.y];
-  const int k = 1 + blockIdx.x;
+  if (T.T == 0) return;
+  const uint32_t k = 1 + blockIdx.x;            // table index 1..16
+  const uint32_t t = k - 1;                     // 2 * (field - 1) + coset
+  const uint32_t c = t & 1u;
+  const uint32_t field = 1 + (t >> 1);
   const uint32_t A = T.alphabet[k];
-  const uint32_t M = 1u << T.b;
-  uint16_t* lut = T.lut + (size_t(k - 1) << T.b);
-  uint32_t* sym = T.symtab + T.sym_base[k];
+  const uint32_t b = T.b;
+  const uint32_t M = 1u << b;
+  const bool narrow = T.variant == kVarN12;               // u8 slot map
+  const uint32_t S = T.variant == kVarGlobal ? M : lds_stride(!narrow);
+  unsigned char* lut8 = T.tab + (size_t(t) << b);
+  uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
+  const size_t lut_bytes = (size_t(16) << b) * (narrow ? 1 : 2);
+  uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lut_bytes) + size_t(t) * S;
+  float* val = reinterpret_cast<float*>(T.tab + lut_bytes + size_t(16) * S * 4) + size_t(t) * S;
   __shared__ uint32_t scan[256];
   __shared__ uint32_t carry;
-  if (A == 0) {
-    for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) lut[j] = 0;
-    if (threadIdx.x == 0) sym[0] = M & 0xFFFFu;   // never used: the decoder flags the tile
+  for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
+    sym[i] = 0;
+    val[i] = 0.0f;
+  }
+  if (A == 0) {   // empty table: never used, the decoder flags the tile
+    for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
+      if (narrow) lut8[j] = 0;
+      else lut16[j] = 0;
+    }
     return;
   }
   if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   const uint16_t* fr = T.freqs + T.freq_base[k];
+  const int32_t mn = T.minv[k];
   for (uint32_t base = 0; base < A; base += blockDim.x) {
     const uint32_t i = base + threadIdx.x;
     const uint32_t f = i < A ? fr[i] : 0u;
@@ -103,7 +154,13 @@ __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __re
       __syncthreads();
     }
     const uint32_t cum = carry + scan[threadIdx.x] - f;
-    if (i < A) sym[i] = (f & 0xFFFFu) | (cum << 16);
+    if (i < A) {
+      // LDS layouts (b <= 12, f <= 4096) keep the parity of the value z in bit 15
+      const uint32_t zpar = (T.variant != kVarGlobal && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
+      sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
+      const float z = float(int32_t(i) + mn);
+      val[i] = field < 8 ? z + 0.5f * float(c) : 2.0f * z + 0.5f * float(c);
+    }
     __syncthreads();
     if (threadIdx.x == blockDim.x - 1) carry += scan[threadIdx.x];
     __syncthreads();
@@ -112,21 +169,16 @@ __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __re
   for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
     uint32_t lo = 0, hi = A;
     while (hi - lo > 1) {
-      uint32_t mid = (lo + hi) >> 1;
-      if ((sym[mid] >> 16) <= j) lo = mid;
+      const uint32_t mid = (lo + hi) >> 1;
+      if ((sym[mid] >> 16) - (c << b) <= j) lo = mid;
       else hi = mid;
     }
-    lut[j] = uint16_t(lo);
+    if (narrow) lut8[j] = uint8_t(lo);
+    else lut16[j] = uint16_t(lo);
   }
 }
 
 // ---------------------------------------------------------------- container rounding
-__device__ __forceinline__ uint32_t bf16_rne(float y) {
-  uint32_t u = __float_as_uint(y);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // OCP e4m3fn: clamp to +-448, then round to nearest even at the format's quantum.
 __device__ __forceinline__ uint32_t fp8_e4m3_rne(float y) {
   const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
@@ -149,166 +201,329 @@ __device__ __forceinline__ uint32_t int8_rne(float y) {
 }
 
 // ---------------------------------------------------------------- decode
-__device__ __forceinline__ uint32_t half_bits(uint64_t bal, int half) {
-  return half ? uint32_t(bal >> 32) : uint32_t(bal);
+// Per-tile payload staging: each half-wave streams its tile's words through an
+// LDS ring of kRingWords, filled kChunkWords at a time (one 8-byte load per
+// lane).  Every vector round issues exactly three memory operations -- the
+// row-scale load, the next ring chunk and the output store -- all as raw
+// buffer operations, whose out-of-range lanes the hardware turns into zero
+// loads and dropped stores.  With a fixed count per round the waits stay
+// precise: waiting for this round's row scale never waits for the chunk in
+// flight behind it.
+constexpr uint32_t kRingWords = 512;
+constexpr uint32_t kChunkWords = 128;
+constexpr uint32_t kRoundWords = 9 * 32;                 // most words one vector round can read
+constexpr uint32_t kRingSlack = kRingWords - kChunkWords; // a chunk fits while fill <= read + slack
+constexpr size_t kRingBytes = size_t(kTilesPerChunk) * kRingWords * sizeof(uint16_t);
+
+enum OutKind : int { kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kNumOutKinds = 4 };
+
+__host__ __device__ constexpr uint32_t out_vec_bytes(int ok) {
+  return ok == kOutBF16 ? 16u : ok == kOutLattice ? 32u : 8u;
 }
 
-__global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
-                                                        const Chunk* __restrict__ chunks) {
-  const Chunk ch = chunks[blockIdx.x];
-  const DevTensor& T = tens[ch.tensor];
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const uint32_t l = lane & 31;
-  const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t t = ch.tile0 + wave * kTilesPerWave + half;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));   // v_cvt_pk_bf16_f32 (RNE)
+}
+
+// Decode the two tiles of one wave (tile0 + 2*wave + half).  BT is the
+// probability precision when known at compile time (0: read T.b); GT selects
+// decode tables in the workspace (u16 slot map, stride 2^b) instead of LDS at
+// address 0 (WIDE: u16 slot map, stride 512; else u8, stride 256); OK is the
+// output kind.
+template <int BT, bool GT, int OK, bool WIDE>
+__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
+                                            const unsigned char* __restrict__ lds,
+                                            uint16_t* __restrict__ ring) {
+  const uint32_t B = BT ? uint32_t(BT) : T.b;
+  const uint32_t M = 1u << B;
+  const uint32_t MASK = M - 1u;
+  const uint32_t S = GT ? M : lds_stride(WIDE);             // sym / val table stride
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t half = lane >> 5;
+  const uint32_t hs = half << 4;                            // selects this half's packed pointer
+  const uint32_t l = lane & 31u;
+  const uint32_t t = tile0 + 2u * (threadIdx.x >> 6) + half;
   const bool tile_ok = t < T.T;
 
-  const uint32_t b = T.b;
-  const uint32_t M = 1u << b;
-  const uint32_t mask = M - 1u;
-  const uint32_t f0 = T.freqs[T.freq_base[0]];   // table 0: frequency of c = 0
-  const uint32_t V = T.V;
-
+  // ---- per-lane tile start
   uint32_t n = 0, x = kL, p = 0, pend = 0;
-  int err = 0;
+  bool bad_len = false;
   if (tile_ok) {
-    const uint64_t first = uint64_t(t) * V;
-    n = uint32_t(min(uint64_t(V), T.nvec - first));
-    x = T.states[size_t(t) * EP_LANES + l];
-    p = T.offsets[t];
-    pend = T.offsets[t + 1];
+    const uint64_t first = uint64_t(t) * T.V;
+    n = uint32_t(min(uint64_t(T.V), T.nvec - first));
+    x = ((const EP_GLOBAL uint32_t*)T.states)[size_t(t) * EP_LANES + l];
+    p = ((const EP_GLOBAL uint32_t*)T.offsets)[t];
+    pend = ((const EP_GLOBAL uint32_t*)T.offsets)[t + 1];
     if (pend < p || pend > T.payload_words) {
-      err = EP_TILE_BAD_LENGTH;
+      bad_len = true;
       n = 0;
+      pend = p;
     }
   }
-  const uint32_t nk = (n + 31u) >> 5;
-  const uint32_t kmax = max(__shfl(nk, 0), __shfl(nk, 32));
+  const __amdgpu_buffer_rsrc_t rP = make_rsrc(T.payload, T.payload_bytes);
+  const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, T.out_bytes);
+  const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.row_scales, T.rows * 4u);
 
-  // position of this lane's first vector: row and vector-in-row
-  uint64_t g = uint64_t(t) * V + l;
+  // ---- per-half-wave uniform state (scalar registers)
+  const uint32_t n0 = __builtin_amdgcn_readlane(n, 0), n1 = __builtin_amdgcn_readlane(n, 32);
+  const uint32_t st0 = __builtin_amdgcn_readlane(p, 0), st1 = __builtin_amdgcn_readlane(p, 32);
+  const uint32_t a00 = st0 & ~3u, a01 = st1 & ~3u;          // 8-byte aligned first word
+  const uint32_t end0 = __builtin_amdgcn_readlane(pend, 0) - a00;
+  const uint32_t end1 = __builtin_amdgcn_readlane(pend, 32) - a01;
+  uint32_t P0 = st0 - a00, P1 = st1 - a01;                  // ring-relative read pointers
+  uint32_t F0 = 0, F1 = 0;                                  // words written to the ring
+  uint64_t empty_err = 0;
+  const uint32_t lane4 = 4u * l;                            // this lane's words inside a chunk
+  const uint32_t chunk_lane = 2u * ((half ? a01 : a00) + lane4);   // byte offset of this lane's part
+  const uint32_t kmax = max((n0 + 31u) >> 5, (n1 + 31u) >> 5);
+
+  const uint32_t f0 = ((const EP_GLOBAL uint16_t*)T.freqs)[T.freq_base[0]];   // coset bit: frequency of c = 0
+  const uint32_t f1 = M - f0;
+  uint32_t f0v = f0, f1v = f1;                                // per-lane copies for selects
+  asm volatile("" : "+v"(f0v), "+v"(f1v));
+  const float scale = T.scale;
+  const uint32_t kpar = T.kpar;
+  const uint32_t empty = T.empty_mask;
+  const unsigned char* gtab = T.tab;
+  const uint32_t lut_bytes = GT ? (32u << B) : uint32_t(lds_lut_bytes(B, WIDE));
+  const unsigned char* tbase = GT ? gtab : lds;
+
+  // the chunk held in registers is always the one starting at word F of the half
+  u32x2 pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane, 0, 0);
+  // A store past the end of the output (dropped by the hardware): it makes the
+  // first round see the same queue of outstanding memory operations as every
+  // later round (chunk, then store), so the compiler's waits stay exact.
+  __builtin_amdgcn_raw_buffer_store_b32(0u, rO, T.out_bytes, 0, 0);
+
+  uint32_t g = t * T.V + l;                                 // < 2^32: checked on the host
   uint32_t row = 0, col = 0;
   if (tile_ok) {
-    row = uint32_t(g / T.vpr);
-    col = uint32_t(g - uint64_t(row) * T.vpr);
+    row = g / T.vpr;
+    col = g - row * T.vpr;
   }
 
   for (uint32_t k = 0; k < kmax; ++k) {
     const bool active = (k * 32u + l) < n;
+    const uint64_t actm = __builtin_amdgcn_ballot_w64(active);
+    const uint32_t x_saved = x;
+    const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
 
-    // field 0: coset bit c (two-symbol table, resolved by one compare)
-    uint32_t slot = x & mask;
-    const uint32_t c = slot >= f0 ? 1u : 0u;
-    if (active) x = (c ? (M - f0) : f0) * (x >> b) + slot - (c ? f0 : 0u);
+    // ---- ring: store the held chunk if it is useful and fits ...
     {
-      const bool need = active && x < kL;
-      const uint32_t hb = half_bits(__ballot(need), half);
-      if (need) {
-        const uint32_t idx = p + __popc(hb & ((1u << l) - 1u));
-        if (idx < pend) x = (x << 16) | T.payload[idx];
-        else err = EP_TILE_OVERRUN;
+      const bool w0 = F0 < end0 && F0 <= P0 + kRingSlack;
+      const bool w1 = F1 < end1 && F1 <= P1 + kRingSlack;
+      // both halves' predicates and fill pointers packed into one scalar each;
+      // a lane extracts its half's 16 bits (tile payloads stay below 2^16 words)
+      const uint32_t wbits = uint32_t(w0) | (uint32_t(w1) << 16);
+      if (__builtin_amdgcn_ubfe(wbits, hs, 1)) {
+        const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
+        *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = pf;
       }
-      p += __popc(hb);
+      F0 += w0 ? kChunkWords : 0u;
+      F1 += w1 ? kChunkWords : 0u;
     }
-    if (active && ((T.empty_mask >> (1u + c)) & 1u)) err = EP_TILE_EMPTY_TABLE;
+    // ... catch up synchronously if this round could read past the staged words
+    // (tile starts, and long runs above kChunkWords words per round) ...
+    for (;;) {
+      const bool c0 = F0 < min(P0 + kRoundWords, end0);
+      const bool c1 = F1 < min(P1 + kRoundWords, end1);
+      if (!(c0 || c1)) break;
+      const uint32_t cbits = uint32_t(c0) | (uint32_t(c1) << 16);
+      if (__builtin_amdgcn_ubfe(cbits, hs, 1)) {
+        const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * F, 0, 0);
+        *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = v;
+      }
+      F0 += c0 ? kChunkWords : 0u;
+      F1 += c1 ? kChunkWords : 0u;
+    }
+    // ... and fetch the chunk at the new fill position for a later round.
+    pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16),
+                                              0, 0);
 
-    int32_t val[9];
+#define EP_RENORM()                                                                   \
+  {                                                                                   \
+    const uint64_t nm = __builtin_amdgcn_ballot_w64(x < kL) & actm;                   \
+    const uint32_t nlo = uint32_t(nm), nhi = uint32_t(nm >> 32);                      \
+    const uint32_t clo = __builtin_popcount(nlo), chi = __builtin_popcount(nhi);      \
+    /* both halves' ring pointers in one scalar: half 1 pre-corrected for the      \
+       half-0 bits that mbcnt_lo also counts; only the low 10 bits matter */        \
+    const uint32_t pk = (P0 & 0xFFFFu) | ((P1 - clo) << 16);                          \
+    if ((x < kL) & active) {                                                          \
+      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(nhi, __builtin_amdgcn_mbcnt_lo(nlo, pk >> hs)); \
+      x = (x << 16) | ring[idx & (kRingWords - 1u)];                                  \
+    }                                                                                 \
+    P0 += clo;                                                                        \
+    P1 += chi;                                                                        \
+  }
+
+    // ---- field 0: coset bit (two-symbol table, resolved by one compare)
+    uint32_t q = x >> B;
+    uint32_t slot = x & MASK;
+    const bool c = slot >= f0v;
+    x = __umul24(c ? f1v : f0v, q) + slot - (c ? f0v : 0u);
+    EP_RENORM();
+    if (empty & 6u) empty_err |= __builtin_amdgcn_ballot_w64(active && ((empty >> (c ? 2 : 1)) & 1u));
+
+    // ---- fields z1..z7, m
+    const uint32_t lb = c ? M : 0u;                 // coset offset inside each table pair
+    // coset table base, including the table block's own offset so that the
+    // per-field offsets fit the 16-bit immediate of the LDS reads
+    uint32_t cb = c ? lut_bytes + S * 4u : lut_bytes;
+    if (!GT) asm volatile("" : "+v"(cb));
+    uint32_t sv[9];
+    float vv[9];
 #pragma unroll
     for (int f = 1; f <= 8; ++f) {
-      const int k0 = 1 + 2 * (f - 1);
-      const uint32_t sbase = c ? T.sym_base[k0 + 1] : T.sym_base[k0];
-      const int32_t mn = c ? T.minv[k0 + 1] : T.minv[k0];
-      const uint16_t* lut = T.lut + (size_t(k0 - 1 + c) << b);
-      slot = x & mask;
-      const uint32_t s = lut[slot];
-      const uint32_t e = T.symtab[sbase + s];
-      if (active) x = (e & 0xFFFFu) * (x >> b) + slot - (e >> 16);
-      val[f] = int32_t(s) + mn;
-      const bool need = active && x < kL;
-      const uint32_t hb = half_bits(__ballot(need), half);
-      if (need) {
-        const uint32_t idx = p + __popc(hb & ((1u << l) - 1u));
-        if (idx < pend) x = (x << 16) | T.payload[idx];
-        else err = EP_TILE_OVERRUN;
-      }
-      p += __popc(hb);
+      const uint32_t addr = (x & MASK) | lb;        // slot + coset * 2^b
+      uint32_t s;
+      if (GT) s = reinterpret_cast<const uint16_t*>(gtab)[(uint32_t(2 * (f - 1)) << B) + addr];
+      else if (WIDE) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr];
+      else s = lds[(uint32_t(2 * (f - 1)) << B) + addr];
+      const uint32_t eo = cb + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
+      const uint32_t e = *reinterpret_cast<const uint32_t*>(tbase + eo);
+      vv[f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
+      q = x >> B;
+      x = __umul24(e & (GT ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
+      sv[f] = GT ? s : e;
+      EP_RENORM();
     }
+#undef EP_RENORM
+    x = active ? x : x_saved;
 
-    if (active) {
-      // algebraic inverse: z8 = 2m + parity(z1..z7), x_i = z_i + c/2
-      int32_t s7 = 0;
+    // ---- reconstruction: z8 = 2m + parity(z1 + ... + z7); the m table holds 2m + c/2
+    const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(sv[1], sv[2], sv[3], 0x96),
+                                                    __builtin_amdgcn_bitop3_b32(sv[4], sv[5], sv[6], 0x96),
+                                                    sv[7], 0x96);
+    // LDS layouts: bit 15 of the entries is the parity of z; workspace layout:
+    // parity of the symbol indices corrected by the parity of the minima
+    const uint32_t par = GT ? ((x3 ^ (kpar >> (c ? 1 : 0))) & 1u) : __builtin_amdgcn_ubfe(x3, 15, 1);
+    vv[8] = vv[8] + float(par);
+    // inactive lanes (past the end of their tile) write past the end of the
+    // output, and the hardware drops the store
+    const uint32_t ob = active ? (g + k * 32u) * out_vec_bytes(OK) : T.out_bytes;
+    if (OK == kOutLattice) {
+      const i32x4 lo4 = {int(2.0f * vv[1]), int(2.0f * vv[2]), int(2.0f * vv[3]), int(2.0f * vv[4])};
+      const i32x4 hi4 = {int(2.0f * vv[5]), int(2.0f * vv[6]), int(2.0f * vv[7]), int(2.0f * vv[8])};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo4), rO, ob, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi4), rO, ob + 16u, 0, 0);
+    } else {
+      const float gs = __fmul_rn(scale, rs);
+      float y[8];
 #pragma unroll
-      for (int i = 1; i <= 7; ++i) s7 += val[i];
-      int32_t z[8];
-#pragma unroll
-      for (int i = 0; i < 7; ++i) z[i] = val[i + 1];
-      z[7] = 2 * val[8] + (s7 & 1);
-      const uint64_t gv = g + uint64_t(k) * 32u;
-      if (T.dtype == EP_OUT_LATTICE2X_I32) {
-        int4* o = reinterpret_cast<int4*>(T.out) + 2 * gv;
-        o[0] = make_int4(2 * z[0] + int(c), 2 * z[1] + int(c), 2 * z[2] + int(c), 2 * z[3] + int(c));
-        o[1] = make_int4(2 * z[4] + int(c), 2 * z[5] + int(c), 2 * z[6] + int(c), 2 * z[7] + int(c));
+      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], gs);
+      if (OK == kOutBF16) {
+        const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                         pack_bf16x2(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
+      } else if (OK == kOutFP8) {
+        const u32x2 w = {fp8_e4m3_rne(y[0]) | (fp8_e4m3_rne(y[1]) << 8) | (fp8_e4m3_rne(y[2]) << 16) |
+                             (fp8_e4m3_rne(y[3]) << 24),
+                         fp8_e4m3_rne(y[4]) | (fp8_e4m3_rne(y[5]) << 8) | (fp8_e4m3_rne(y[6]) << 16) |
+                             (fp8_e4m3_rne(y[7]) << 24)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       } else {
-        const float gs = __fmul_rn(T.scale, T.row_scales[row]);
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float xi = __fmul_rn(float(2 * z[i] + int(c)), 0.5f);   // exact half-integer
-          y[i] = __fmul_rn(xi, gs);
-        }
-        if (T.dtype == EP_OUT_BF16) {
-          uint4 w;
-          w.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
-          w.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
-          w.z = bf16_rne(y[4]) | (bf16_rne(y[5]) << 16);
-          w.w = bf16_rne(y[6]) | (bf16_rne(y[7]) << 16);
-          reinterpret_cast<uint4*>(T.out)[gv] = w;
-        } else if (T.dtype == EP_OUT_FP8_E4M3) {
-          uint2 w;
-          w.x = fp8_e4m3_rne(y[0]) | (fp8_e4m3_rne(y[1]) << 8) | (fp8_e4m3_rne(y[2]) << 16) |
-                (fp8_e4m3_rne(y[3]) << 24);
-          w.y = fp8_e4m3_rne(y[4]) | (fp8_e4m3_rne(y[5]) << 8) | (fp8_e4m3_rne(y[6]) << 16) |
-                (fp8_e4m3_rne(y[7]) << 24);
-          reinterpret_cast<uint2*>(T.out)[gv] = w;
-        } else {
-          uint2 w;
-          w.x = int8_rne(y[0]) | (int8_rne(y[1]) << 8) | (int8_rne(y[2]) << 16) | (int8_rne(y[3]) << 24);
-          w.y = int8_rne(y[4]) | (int8_rne(y[5]) << 8) | (int8_rne(y[6]) << 16) | (int8_rne(y[7]) << 24);
-          reinterpret_cast<uint2*>(T.out)[gv] = w;
-        }
+        const u32x2 w = {int8_rne(y[0]) | (int8_rne(y[1]) << 8) | (int8_rne(y[2]) << 16) | (int8_rne(y[3]) << 24),
+                         int8_rne(y[4]) | (int8_rne(y[5]) << 8) | (int8_rne(y[6]) << 16) | (int8_rne(y[7]) << 24)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       }
     }
-    // advance this lane's vector by 32 positions
     col += 32u;
-    while (col >= T.vpr && T.vpr) {
+    if (col >= T.vpr) {                     // rows of at least 32 vectors wrap at most once
       col -= T.vpr;
       ++row;
+      while (col >= T.vpr) {
+        col -= T.vpr;
+        ++row;
+      }
     }
   }
 
-  // end-of-tile invariants: every state back at 2^15 and every word consumed
-  const uint32_t ov = half_bits(__ballot(err == EP_TILE_OVERRUN), half);
-  const uint32_t et = half_bits(__ballot(err == EP_TILE_EMPTY_TABLE), half);
-  const uint32_t bl = half_bits(__ballot(err == EP_TILE_BAD_LENGTH), half);
-  const uint32_t bs = half_bits(__ballot(x != kL), half);
+  // ---- end-of-tile invariants: every state back at 2^15, every word consumed
+  const uint64_t bad_state = __builtin_amdgcn_ballot_w64(x != kL);
+  const uint64_t bad_len_m = __builtin_amdgcn_ballot_w64(bad_len);
   if (tile_ok && l == 0 && T.status) {
+    const uint32_t Pm = half ? P1 : P0, Em = half ? end1 : end0;
+    const uint32_t sh = half ? 32u : 0u;
     int st = EP_TILE_OK;
-    if (ov) st = EP_TILE_OVERRUN;
-    else if (et) st = EP_TILE_EMPTY_TABLE;
-    else if (bl) st = EP_TILE_BAD_LENGTH;
-    else if (bs) st = EP_TILE_BAD_STATE;
-    else if (p != pend) st = EP_TILE_BAD_LENGTH;
-    T.status[t] = st;
+    if (uint32_t(bad_len_m >> sh)) st = EP_TILE_BAD_LENGTH;
+    else if (Pm > Em) st = EP_TILE_OVERRUN;
+    else if (uint32_t(empty_err >> sh)) st = EP_TILE_EMPTY_TABLE;
+    else if (uint32_t(bad_state >> sh)) st = EP_TILE_BAD_STATE;
+    else if (Pm != Em) st = EP_TILE_BAD_LENGTH;
+    ((EP_GLOBAL int32_t*)T.status)[t] = st;
+  }
+}
+
+// Persistent decode kernel: block i walks a contiguous range of chunks (32 tiles
+// of one tensor each).  LDS variants stage the tensor's decode tables once per
+// run of chunks from the same tensor.
+template <int BT, bool GT, int OK, bool WIDE>
+__global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
+                                                        const Chunk* __restrict__ chunks,
+                                                        uint32_t nchunks) {
+  __shared__ __align__(16) unsigned char smem[(GT ? 0 : lds_table_bytes(BT, WIDE)) + kRingBytes];
+  const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
+  const uint32_t c0 = blockIdx.x * per;
+  const uint32_t c1 = min(nchunks, c0 + per);
+  // LDS: [decode tables (LDS variants)][32 rings of kRingWords]
+  const uint32_t ring_off = GT ? 0u : uint32_t(lds_table_bytes(BT, WIDE));
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + ring_off) + (threadIdx.x >> 5) * kRingWords;
+  uint32_t cur = 0xFFFFFFFFu;
+  for (uint32_t ci = c0; ci < c1; ++ci) {
+    const Chunk ch = chunks[ci];
+    const DevTensor& T = tens[ch.tensor];
+    if (!GT && ch.tensor != cur) {
+      __syncthreads();
+      const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)T.tab;
+      u32x4* dst = reinterpret_cast<u32x4*>(smem);
+      for (uint32_t i = threadIdx.x; i < T.tab_bytes / 16u; i += kBlock) dst[i] = src[i];
+      __syncthreads();
+    }
+    cur = ch.tensor;
+    decode_pair<BT, GT, OK, WIDE>(T, ch.tile0, smem, ring);
   }
 }
 
 // ---------------------------------------------------------------- host side
+
+uint32_t choose_variant(const ep_tensor_desc& d) {
+  uint32_t amax = 0;
+  for (int k = 1; k < kTables; ++k) amax = std::max(amax, d.alphabet[k]);
+  if (d.prob_bits <= 11 && amax <= lds_stride(true) && lds_table_bytes(d.prob_bits, true) + kRingBytes <= kMaxLds)
+    return kVarW9 + (d.prob_bits - 9);
+  if (d.prob_bits == 12 && amax <= lds_stride(false) && lds_table_bytes(12, false) + kRingBytes <= kMaxLds)
+    return kVarN12;
+  return kVarGlobal;
+}
+
+
+constexpr uint32_t kNumGroups = kNumVariants * kNumOutKinds;   // one launch per non-empty group
+
+int out_kind_of(int dtype) {
+  switch (dtype) {
+    case EP_OUT_BF16: return kOutBF16;
+    case EP_OUT_FP8_E4M3: return kOutFP8;
+    case EP_OUT_INT8: return kOutINT8;
+    case EP_OUT_LATTICE2X_I32: return kOutLattice;
+    default: return -1;
+  }
+}
+
 struct Layout {
   size_t tens_off, chunk_off, total;
-  std::vector<size_t> lut_off, sym_off;
-  std::vector<uint32_t> sym_count;
+  std::vector<size_t> tab_off, tab_bytes;
+  std::vector<uint32_t> variant, group;
   size_t nchunks;
+  size_t group_chunks[kNumGroups];
 };
 
 int validate(const ep_tensor_desc& d, int i) {
@@ -318,6 +533,8 @@ int validate(const ep_tensor_desc& d, int i) {
   if (d.rows < 0) return bad("rows < 0");
   if (d.cols <= 0 || d.cols % 8 != 0) return bad("cols must be a positive multiple of 8");
   if (d.vectors_per_tile < 32) return bad("vectors_per_tile < 32");
+  // a tile's payload (at most 9 words per vector) is addressed with 16-bit offsets
+  if (d.vectors_per_tile > 7200) return bad("vectors_per_tile > 7200");
   if (d.prob_bits < 9 || d.prob_bits > 15) return bad("prob_bits outside [9, 15]");
   const unsigned __int128 nvec = (unsigned __int128)(uint64_t)d.rows * (uint64_t)d.cols / 8u;
   if (nvec >= ((unsigned __int128)1 << 32)) return bad("rows*cols/8 must be < 2^32");
@@ -327,52 +544,108 @@ int validate(const ep_tensor_desc& d, int i) {
   if (d.alphabet[0] != 2 || d.min_offset[0] != 0) return bad("table 0 must be the coset bit (alphabet 2, min 0)");
   for (int k = 1; k < kTables; ++k)
     if (d.alphabet[k] > (1u << d.prob_bits)) return bad("alphabet exceeds 2^prob_bits");
+  if (2 * ((d.payload_words + 7) / 8 * 8) >= (uint64_t(1) << 32)) return bad("payload must be < 4 GiB");
+  // 32-bit output offsets: every vector a tile's lanes can address stays below 2^32 bytes
+  if ((nv + 64ull * d.vectors_per_tile + 64) * 32ull >= (uint64_t(1) << 32))
+    return bad("tensor too large for one descriptor (split it)");
   if (d.num_tiles > 0) {
     if (!d.row_scales || !d.tile_states || !d.tile_offsets || !d.payload || !d.freqs)
       return bad("NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(d.payload) % 16 != 0) return bad("payload must be 16-byte aligned");
   }
   return EP_OK;
 }
 
-int make_layout(const ep_tensor_desc* descs, int n, Layout& L) {
+int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L) {
   if (n < 0 || (n > 0 && !descs)) return fail(EP_ERR_INVALID_ARG, "bad tensor count or NULL descriptors");
   size_t off = 0;
   L.tens_off = off;
   off = align256(off + sizeof(DevTensor) * size_t(n));
   L.nchunks = 0;
+  L.tab_off.resize(n);
+  L.tab_bytes.resize(n);
+  L.variant.resize(n);
+  L.group.resize(n);
+  for (uint32_t v = 0; v < kNumGroups; ++v) L.group_chunks[v] = 0;
   for (int i = 0; i < n; ++i) {
     int rc = validate(descs[i], i);
     if (rc != EP_OK) return rc;
-    L.nchunks += (descs[i].num_tiles + kTilesPerChunk - 1) / kTilesPerChunk;
+    const ep_tensor_desc& d = descs[i];
+    const int ok = dtypes ? out_kind_of(dtypes[i]) : kOutBF16;
+    if (ok < 0) return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": unknown output dtype");
+    L.variant[i] = choose_variant(d);
+    L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
+    L.tab_bytes[i] = L.variant[i] == kVarGlobal ? global_table_bytes(d.prob_bits)
+                                                : lds_table_bytes(d.prob_bits, L.variant[i] != kVarN12);
+    const size_t nc = (d.num_tiles + kTilesPerChunk - 1) / kTilesPerChunk;
+    L.nchunks += nc;
+    L.group_chunks[L.group[i]] += nc;
   }
   if (L.nchunks >= (size_t(1) << 31)) return fail(EP_ERR_UNSUPPORTED, "too many tiles in one call");
   L.chunk_off = off;
   off = align256(off + sizeof(Chunk) * L.nchunks);
-  L.lut_off.resize(n);
-  L.sym_off.resize(n);
-  L.sym_count.resize(n);
   for (int i = 0; i < n; ++i) {
-    const ep_tensor_desc& d = descs[i];
-    L.lut_off[i] = off;
-    off = align256(off + sizeof(uint16_t) * (size_t(16) << d.prob_bits));
-    uint32_t cnt = 0;
-    for (int k = 1; k < kTables; ++k) cnt += std::max<uint32_t>(d.alphabet[k], 1u);
-    L.sym_count[i] = cnt;
-    L.sym_off[i] = off;
-    off = align256(off + sizeof(uint32_t) * cnt);
+    L.tab_off[i] = off;
+    off = align256(off + (descs[i].num_tiles ? L.tab_bytes[i] : 0));
   }
   L.total = std::max<size_t>(off, 256);
   return EP_OK;
 }
 
+struct Group {
+  uint32_t chunk_begin, nchunks, lds, grid;
+};
+
 struct PlanImpl {
   void* ws;
-  uint64_t nchunks;
-  uint64_t ntensors;
   uint64_t magic;
+  uint64_t ntensors;
+  Group groups[kNumGroups];
 };
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
-constexpr uint64_t kPlanMagic = 0x45504c414e763031ull;
+constexpr uint64_t kPlanMagic = 0x45504c414e763033ull;
+
+using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t);
+
+template <int BT, bool GT, bool WIDE>
+KernelFn kernel_for_kind(int ok) {
+  switch (ok) {
+    case kOutBF16: return decode_kernel<BT, GT, kOutBF16, WIDE>;
+    case kOutFP8: return decode_kernel<BT, GT, kOutFP8, WIDE>;
+    case kOutINT8: return decode_kernel<BT, GT, kOutINT8, WIDE>;
+    default: return decode_kernel<BT, GT, kOutLattice, WIDE>;
+  }
+}
+
+KernelFn kernel_of(uint32_t group) {
+  const int ok = int(group % kNumOutKinds);
+  switch (group / kNumOutKinds) {
+    case kVarW9: return kernel_for_kind<9, false, true>(ok);
+    case kVarW10: return kernel_for_kind<10, false, true>(ok);
+    case kVarW11: return kernel_for_kind<11, false, true>(ok);
+    case kVarN12: return kernel_for_kind<12, false, false>(ok);
+    default: return kernel_for_kind<0, true, true>(ok);
+  }
+}
+
+// Persistent grid: as many blocks as can be resident at once (at least one).
+int resident_grid(uint32_t v, uint32_t nchunks, uint32_t* grid) {
+  static int cus = 0;
+  hipError_t e;
+  if (cus == 0) {
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("device query: ") + hipGetErrorString(e));
+  }
+  KernelFn fn = kernel_of(v);
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, 0);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
+  const uint64_t g = uint64_t(std::max(per_cu, 1)) * uint64_t(std::max(cus, 1));
+  *grid = uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(g, nchunks)));
+  return EP_OK;
+}
 
 }  // namespace
 
@@ -396,7 +669,7 @@ int ep_abi_version(void) { return EP_ABI_VERSION; }
 int ep_workspace_size(const ep_tensor_desc* descs, int n, size_t* bytes) {
   if (!bytes) return fail(EP_ERR_INVALID_ARG, "bytes is NULL");
   Layout L;
-  int rc = make_layout(descs, n, L);
+  int rc = make_layout(descs, nullptr, n, L);
   if (rc != EP_OK) return rc;
   *bytes = L.total;
   return EP_OK;
@@ -407,20 +680,36 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
                      void* stream, ep_batch_plan* plan) {
   if (!plan) return fail(EP_ERR_INVALID_ARG, "plan is NULL");
   std::memset(plan, 0, sizeof(*plan));
-  Layout L;
-  int rc = make_layout(descs, n, L);
-  if (rc != EP_OK) return rc;
   if (n > 0 && (!dtypes || !outs)) return fail(EP_ERR_INVALID_ARG, "NULL dtypes or outs");
+  Layout L;
+  int rc = make_layout(descs, dtypes, n, L);
+  if (rc != EP_OK) return rc;
   if (!workspace || ws_bytes < L.total)
     return fail(EP_ERR_WORKSPACE, "workspace smaller than ep_workspace_size()");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
-  std::vector<unsigned char> host(L.lut_off.empty() ? L.total : L.lut_off[0], 0);
+  std::vector<unsigned char> host(L.tab_off.empty() ? L.total : L.tab_off[0], 0);
   DevTensor* ht = reinterpret_cast<DevTensor*>(host.data() + L.tens_off);
   Chunk* hc = reinterpret_cast<Chunk*>(host.data() + L.chunk_off);
   char* wsb = static_cast<char*>(workspace);
-  size_t ci = 0;
+  // chunks are grouped by table placement; each group is one kernel launch
+  size_t group_pos[kNumGroups];
+  for (size_t v = 0, acc = 0; v < kNumGroups; ++v) {
+    group_pos[v] = acc;
+    acc += L.group_chunks[v];
+  }
+  PlanImpl* P = reinterpret_cast<PlanImpl*>(plan);
+  for (uint32_t v = 0; v < kNumGroups; ++v) {
+    P->groups[v].chunk_begin = uint32_t(group_pos[v]);
+    P->groups[v].nchunks = uint32_t(L.group_chunks[v]);
+    P->groups[v].lds = 0;
+    P->groups[v].grid = 0;
+    if (L.group_chunks[v]) {
+      rc = resident_grid(v, uint32_t(L.group_chunks[v]), &P->groups[v].grid);
+      if (rc != EP_OK) return rc;
+    }
+  }
   for (int i = 0; i < n; ++i) {
     const ep_tensor_desc& d = descs[i];
     const int dt = dtypes[i];
@@ -435,33 +724,38 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.V = d.vectors_per_tile;
     D.T = d.num_tiles;
     D.b = d.prob_bits;
+    D.rows = uint32_t(d.rows);
     D.scale = d.scale;
     D.dtype = dt;
+    D.variant = L.variant[i];
+    D.tab_bytes = uint32_t(L.tab_bytes[i]);
     D.row_scales = d.row_scales;
     D.states = d.tile_states;
     D.offsets = d.tile_offsets;
     D.payload = d.payload;
     D.payload_words = d.payload_words;
+    D.payload_bytes = uint32_t(2 * ((d.payload_words + 7) / 8 * 8));
+    D.out_bytes = uint32_t(D.nvec * out_vec_bytes(out_kind_of(dt)));
     D.freqs = d.freqs;
-    D.lut = reinterpret_cast<uint16_t*>(wsb + L.lut_off[i]);
-    D.symtab = reinterpret_cast<uint32_t*>(wsb + L.sym_off[i]);
+    D.tab = reinterpret_cast<unsigned char*>(wsb + L.tab_off[i]);
     D.out = outs[i];
     D.status = tile_status ? tile_status[i] : nullptr;
-    uint32_t sb = 0, em = 0;
+    uint32_t em = 0, kpar = 0;
     for (int k = 0; k < kTables; ++k) {
       D.alphabet[k] = d.alphabet[k];
       D.freq_base[k] = d.freq_base[k];
       D.minv[k] = d.min_offset[k];
-      if (k == 0) {
-        D.sym_base[k] = 0;
-        continue;
-      }
-      D.sym_base[k] = sb;
-      sb += std::max<uint32_t>(d.alphabet[k], 1u);
-      if (d.alphabet[k] == 0) em |= 1u << k;
+      if (k > 0 && d.alphabet[k] == 0) em |= 1u << k;
+    }
+    for (int c = 0; c < 2; ++c) {
+      int64_t sum = 0;
+      for (int f = 1; f <= 7; ++f) sum += d.min_offset[1 + 2 * (f - 1) + c];
+      kpar |= uint32_t(sum & 1) << c;
     }
     D.empty_mask = em;
-    for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += kTilesPerChunk) hc[ci++] = Chunk{uint32_t(i), t0};
+    D.kpar = kpar;
+    for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += kTilesPerChunk)
+      hc[group_pos[L.group[i]]++] = Chunk{uint32_t(i), t0};
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
@@ -472,12 +766,9 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
   }
-  PlanImpl* P = reinterpret_cast<PlanImpl*>(plan);
   P->ws = workspace;
-  P->nchunks = L.nchunks;
   P->ntensors = uint64_t(n);
   P->magic = kPlanMagic;
-  (void)ws_bytes;
   return EP_OK;
 }
 
@@ -485,14 +776,17 @@ int ep_batch_launch(const ep_batch_plan* plan, void* stream) {
   if (!plan) return fail(EP_ERR_INVALID_ARG, "plan is NULL");
   const PlanImpl* P = reinterpret_cast<const PlanImpl*>(plan);
   if (P->magic != kPlanMagic) return fail(EP_ERR_INVALID_ARG, "plan was not filled by ep_batch_prepare");
-  if (P->nchunks == 0) return EP_OK;
   char* wsb = static_cast<char*>(P->ws);
-  const size_t chunk_off = align256(sizeof(DevTensor) * size_t(P->ntensors));
-  hipLaunchKernelGGL(decode_kernel, dim3(uint32_t(P->nchunks)), dim3(kBlock), 0,
-                     static_cast<hipStream_t>(stream), reinterpret_cast<const DevTensor*>(wsb),
-                     reinterpret_cast<const Chunk*>(wsb + chunk_off));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  const DevTensor* tens = reinterpret_cast<const DevTensor*>(wsb);
+  const Chunk* chunks = reinterpret_cast<const Chunk*>(wsb + align256(sizeof(DevTensor) * size_t(P->ntensors)));
+  for (uint32_t v = 0; v < kNumGroups; ++v) {
+    const Group& G = P->groups[v];
+    if (G.nchunks == 0) continue;
+    hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
+                       tens, chunks + G.chunk_begin, G.nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  }
   return EP_OK;
 }
 

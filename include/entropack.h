@@ -14,7 +14,7 @@
  * the fields is this library's, the pages print none):
  *   - tensor [rows, cols] row-major, cols % 8 == 0; vector g covers
  *     elements 8g .. 8g+7 of the flattened tensor (blocks of eight weights);
- *   - tiles of V vectors (V >= 32), num_tiles = ceil(rows*cols/8 / V); the
+ *   - tiles of V vectors (32 <= V <= 7200), num_tiles = ceil(rows*cols/8 / V); the
  *     last tile may be partial; tiles may cross row boundaries;
  *   - per tile: 32 u32 terminal rANS states (lane order) and a u32 offset of
  *     the tile's 16-bit payload words; one final offset closes the payload;
@@ -85,16 +85,17 @@ typedef enum {
 /* One compressed tensor.  Pointers are device pointers. */
 typedef struct {
   int64_t rows;                       /* >= 0 */
-  int64_t cols;                       /* > 0, multiple of 8; rows*cols/8 < 2^32 */
-  uint32_t vectors_per_tile;          /* V >= 32 */
+  int64_t cols;                       /* > 0, multiple of 8; (rows*cols/8 + 64*V + 64) * 32 < 2^32 */
+  uint32_t vectors_per_tile;          /* 32 <= V <= 7200 */
   uint32_t num_tiles;                 /* must equal ceil(rows*cols/8 / V) */
   uint32_t prob_bits;                 /* b in [9, 15] */
   float scale;                        /* per-tensor quantisation scale s */
   const float* row_scales;            /* [rows] fitted FP32 row scales */
   const uint32_t* tile_states;        /* [num_tiles * 32] terminal states, lane order */
   const uint32_t* tile_offsets;       /* [num_tiles + 1] offsets in 16-bit words, nondecreasing */
-  const uint16_t* payload;            /* [payload_words] words */
-  uint64_t payload_words;             /* words readable at payload; reads never reach past it */
+  const uint16_t* payload;            /* [payload_words] words, 16-byte aligned; the buffer must be
+                                         readable up to payload_words rounded up to a multiple of 8 */
+  uint64_t payload_words;             /* words in the payload; tile ranges beyond it are flagged */
   const uint16_t* freqs;              /* the 17 tables' frequencies, table k at freq_base[k] */
   uint32_t freq_base[EP_NUM_TABLES];  /* start of table k in freqs */
   uint32_t alphabet[EP_NUM_TABLES];   /* A_k <= 2^b; alphabet[0] == 2; 0 = empty table */
@@ -146,7 +147,7 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
  * workspace.
  */
 typedef struct {
-  uint64_t opaque[16];
+  uint64_t opaque[64];
 } ep_batch_plan;
 
 int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const* outs,
