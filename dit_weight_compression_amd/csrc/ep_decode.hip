@@ -9,11 +9,13 @@
 //
 // Mapping: one wave64 decodes two tiles, one per half-wave; lane l of a half
 // owns the tile's rANS state l (the paper assigns one tile per 32-lane warp and
-// one state per lane).  Renormalisation reads of a half-wave are located with
-// a wave ballot and per-half popcounts, so the lanes that need a word read
-// consecutive payload words.  Each lane reconstructs whole 8-wide vectors and
-// writes them with one 16-byte (BF16) or 8-byte (FP8/INT8) store; the 32 lanes
-// of a half write 512 (256) contiguous bytes.
+// one state per lane).  Workgroups of 16 waves are persistent and keep the
+// current tensor's decode tables in LDS; each tile streams its payload words
+// through a small LDS ring.  Renormalisation reads of a half-wave are located
+// with a wave ballot and mbcnt, so the lanes that need a word read consecutive
+// ring positions.  Each lane reconstructs whole 8-wide vectors and writes them
+// with one 16-byte (BF16) or 8-byte (FP8/INT8) buffer store; the 32 lanes of a
+// half write 512 (256) contiguous bytes.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -29,6 +31,7 @@
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -40,11 +43,32 @@ constexpr int kBlock = 64 * kWavesPerBlock;
 constexpr int kTilesPerChunk = kTilesPerWave * kWavesPerBlock;
 constexpr size_t kMaxLds = 160 * 1024;
 
-// Where a tensor's decode tables live while it is decoded: LDS with the
-// precision compiled in -- "wide" u16 slot maps for b = 9..11 and alphabets up
-// to 512, "narrow" u8 slot maps for b = 12 and alphabets up to 256 -- or the
-// workspace for everything else.
-enum Variant : uint32_t { kVarW9 = 0, kVarW10, kVarW11, kVarN12, kVarGlobal, kNumVariants };
+// ---------------------------------------------------------------- decode tables
+// Three layouts of a tensor's coordinate tables t = 2*(field-1) + coset:
+//   packed    (LDS, b <= 11, alphabets <= 512): one u32 per slot of each table,
+//             (slot - cum) | f << 11 | symbol << 23, so that the state update
+//             is one multiply-add after a single lookup; the symbol's value
+//             follows from the entry and a per-table constant (kvals).
+//   narrow    (LDS, b = 12, alphabets <= 256): u8 slot -> symbol maps, then per
+//             symbol u32 f | (cum + coset*2^b) << 16 (bit 15: parity of z) and
+//             the float value 2 z + c (4 m + c for m), at stride 256.
+//   workspace (anything else): the narrow scheme with u16 slot maps and stride
+//             2^b, read from the workspace through the caches.
+enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2 };
+enum Variant : uint32_t { kVarP9 = 0, kVarP10, kVarP11, kVarN12, kVarWs, kNumVariants };
+
+__host__ __device__ constexpr int layout_of(uint32_t v) {
+  return v <= kVarP11 ? kTabPacked : v == kVarN12 ? kTabNarrow : kTabWorkspace;
+}
+__host__ __device__ constexpr uint32_t stride_of(int tl, uint32_t b) {
+  return tl == kTabNarrow ? 256u : tl == kTabWorkspace ? (1u << b) : 0u;
+}
+__host__ __device__ constexpr size_t lut_bytes_of(int tl, uint32_t b) {
+  return (size_t(16) << b) * (tl == kTabPacked ? 4 : tl == kTabNarrow ? 1 : 2);
+}
+__host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
+  return lut_bytes_of(tl, b) + 2 * size_t(16) * stride_of(tl, b) * 4;
+}
 
 // Device-side view of one tensor (lives in the workspace).
 struct alignas(16) DevTensor {
@@ -54,21 +78,27 @@ struct alignas(16) DevTensor {
   uint32_t rows;
   float scale;
   uint32_t empty_mask;       // bit k: table k is empty
-  int32_t dtype;
   uint32_t variant;          // decode-table placement, see Variant
-  uint32_t kpar;             // bit c: parity of min_offset of fields z1..z7 in coset c
-  uint32_t tab_bytes;        // bytes of the table block copied to LDS (LDS variants)
+  uint32_t kpar;             // bit c: parity of the minima of fields z1..z7 in coset c
+  uint32_t tab_bytes;        // bytes of the table block
+  uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
+  uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
+  uint32_t slow_rows;        // set by the table build: rowv holds g, not g/2
+  uint32_t pad0;
+  uint64_t payload_words;
   const float* row_scales;
+  float* rowv;               // workspace: per-row multiplier g/2 (or g), g = fp32(scale * row scale)
   const uint32_t* states;
   const uint32_t* offsets;
   const uint16_t* payload;
-  uint64_t payload_words;
-  uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
-  uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
   const uint16_t* freqs;
-  unsigned char* tab;        // workspace: decode tables, layout per variant
+  unsigned char* tab;        // workspace: decode tables in the variant's layout
   void* out;
   int32_t* status;
+  // packed layout, value constants as fp32 bit patterns, indexed by table t:
+  // t < 14: 2^23 + 2^22 + [f = 2^11] - (2 min_t + c), t = 14, 15: 2^23 + 2^22 - 4 min_t,
+  // t = 16, 17: parity of the minima of z1..z7 in coset t - 16, at bit 23
+  uint32_t kvals[32];
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
   uint32_t alphabet[kTables];
@@ -88,29 +118,31 @@ int fail(int code, const std::string& msg) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Decode-table layout.  For coordinate table t = 2*(field-1) + coset (16 of them):
-//   lut   [16][2^b]   slot -> zero-based symbol (u8 in the narrow LDS layout, u16 otherwise)
-//   sym   [16][S]     f | (cum + coset * 2^b) << 16   (S = 256 narrow, 512 wide, 2^b workspace);
-//                     in the LDS layouts bit 15 also holds the parity of the value of z1..z7
-//   val   [16][S]     float value the symbol stands for: z + c/2 for z1..z7, 2m + c/2 for m
-// Adding coset * 2^b to cum lets the decoder subtract the coset-offset slot directly.
-__host__ __device__ constexpr uint32_t lds_stride(bool wide) { return wide ? 512u : 256u; }
-__host__ __device__ constexpr size_t lds_lut_bytes(uint32_t b, bool wide) {
-  return (size_t(16) << b) * (wide ? 2 : 1);
-}
-__host__ __device__ constexpr size_t lds_table_bytes(uint32_t b, bool wide) {
-  return lds_lut_bytes(b, wide) + 2 * size_t(16) * lds_stride(wide) * 4;
-}
-__host__ __device__ constexpr size_t global_table_bytes(uint32_t b) {
-  return (size_t(16) << b) * 2 + 2 * (size_t(16) << b) * 4;
-}
-
 // ---------------------------------------------------------------- table build
 // One block per (coordinate table, tensor): cumulative frequencies by a block
 // scan, then the slot -> symbol map by a binary search per slot.
-__global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __restrict__ tens) {
-  const DevTensor& T = tens[blockIdx.y];
+__global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens) {
+  DevTensor& T = tens[blockIdx.y];
   if (T.T == 0) return;
+  if (blockIdx.x == 16) {
+    // per-row multipliers.  (2 z + c) * (g / 2) equals (z + c/2) * g exactly
+    // whenever g / 2 is exact; a tensor with any row where it is not keeps g.
+    __shared__ uint32_t inexact;
+    if (threadIdx.x == 0) inexact = 0;
+    __syncthreads();
+    for (uint32_t r = threadIdx.x; r < T.rows; r += blockDim.x) {
+      const float gr = __fmul_rn(T.scale, T.row_scales[r]);
+      if (!(__fmul_rn(__fmul_rn(gr, 0.5f), 2.0f) == gr)) inexact = 1;
+    }
+    __syncthreads();
+    const bool slow = inexact != 0;
+    for (uint32_t r = threadIdx.x; r < T.rows; r += blockDim.x) {
+      const float gr = __fmul_rn(T.scale, T.row_scales[r]);
+      T.rowv[r] = slow ? gr : __fmul_rn(gr, 0.5f);
+    }
+    if (threadIdx.x == 0) T.slow_rows = slow ? 1u : 0u;
+    return;
+  }
   const uint32_t k = 1 + blockIdx.x;            // table index 1..16
   const uint32_t t = k - 1;                     // 2 * (field - 1) + coset
   const uint32_t c = t & 1u;
@@ -118,22 +150,27 @@ __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __re
   const uint32_t A = T.alphabet[k];
   const uint32_t b = T.b;
   const uint32_t M = 1u << b;
-  const bool narrow = T.variant == kVarN12;               // u8 slot map
-  const uint32_t S = T.variant == kVarGlobal ? M : lds_stride(!narrow);
+  const int tl = layout_of(T.variant);
+  const uint32_t S = stride_of(tl, b);
   unsigned char* lut8 = T.tab + (size_t(t) << b);
   uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
-  const size_t lut_bytes = (size_t(16) << b) * (narrow ? 1 : 2);
-  uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lut_bytes) + size_t(t) * S;
-  float* val = reinterpret_cast<float*>(T.tab + lut_bytes + size_t(16) * S * 4) + size_t(t) * S;
+  uint32_t* lut32 = reinterpret_cast<uint32_t*>(T.tab) + (size_t(t) << b);
+  const size_t lb = lut_bytes_of(tl, b);
+  uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
+  float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
   __shared__ uint32_t scan[256];
+  __shared__ uint32_t cums[512];               // packed layout: f | cum << 16 per symbol
   __shared__ uint32_t carry;
-  for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
-    sym[i] = 0;
-    val[i] = 0.0f;
+  if (tl != kTabPacked) {
+    for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
+      sym[i] = 0;
+      val[i] = 0.0f;
+    }
   }
   if (A == 0) {   // empty table: never used, the decoder flags the tile
     for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
-      if (narrow) lut8[j] = 0;
+      if (tl == kTabPacked) lut32[j] = 1u << 11;   // f = 1, slot - cum = 0, symbol 0
+      else if (tl == kTabNarrow) lut8[j] = 0;
       else lut16[j] = 0;
     }
     return;
@@ -155,11 +192,15 @@ __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __re
     }
     const uint32_t cum = carry + scan[threadIdx.x] - f;
     if (i < A) {
-      // LDS layouts (b <= 12, f <= 4096) keep the parity of the value z in bit 15
-      const uint32_t zpar = (T.variant != kVarGlobal && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
-      sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
-      const float z = float(int32_t(i) + mn);
-      val[i] = field < 8 ? z + 0.5f * float(c) : 2.0f * z + 0.5f * float(c);
+      if (tl == kTabPacked) {
+        cums[i] = (f & 0xFFFFu) | (cum << 16);
+      } else {
+        // the narrow layout (b = 12, f <= 4096) keeps the parity of the value z in bit 15
+        const uint32_t zpar = (tl == kTabNarrow && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
+        sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
+        const int32_t z = int32_t(i) + mn;
+        val[i] = float(field < 8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
+      }
     }
     __syncthreads();
     if (threadIdx.x == blockDim.x - 1) carry += scan[threadIdx.x];
@@ -170,11 +211,18 @@ __global__ __launch_bounds__(256) void build_tables_kernel(const DevTensor* __re
     uint32_t lo = 0, hi = A;
     while (hi - lo > 1) {
       const uint32_t mid = (lo + hi) >> 1;
-      if ((sym[mid] >> 16) - (c << b) <= j) lo = mid;
+      const uint32_t cm = tl == kTabPacked ? (cums[mid] >> 16) : (sym[mid] >> 16) - (c << b);
+      if (cm <= j) lo = mid;
       else hi = mid;
     }
-    if (narrow) lut8[j] = uint8_t(lo);
-    else lut16[j] = uint16_t(lo);
+    if (tl == kTabPacked) {
+      const uint32_t e = cums[lo];
+      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | (lo << 23);
+    } else if (tl == kTabNarrow) {
+      lut8[j] = uint8_t(lo);
+    } else {
+      lut16[j] = uint16_t(lo);
+    }
   }
 }
 
@@ -198,6 +246,14 @@ __device__ __forceinline__ uint32_t int8_rne(float y) {
   float r = __builtin_rintf(y);
   r = fminf(fmaxf(r, -128.0f), 127.0f);
   return uint32_t(int32_t(r)) & 0xFFu;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));   // v_cvt_pk_bf16_f32 (RNE)
 }
 
 // ---------------------------------------------------------------- decode
@@ -225,30 +281,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const float2_t f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));   // v_cvt_pk_bf16_f32 (RNE)
-}
-
 // Decode the two tiles of one wave (tile0 + 2*wave + half).  BT is the
-// probability precision when known at compile time (0: read T.b); GT selects
-// decode tables in the workspace (u16 slot map, stride 2^b) instead of LDS at
-// address 0 (WIDE: u16 slot map, stride 512; else u8, stride 256); OK is the
-// output kind.
-template <int BT, bool GT, int OK, bool WIDE>
+// probability precision when known at compile time (0: read T.b), TL the
+// table layout (LDS tables start at LDS address 0), OK the output kind.
+template <int BT, int TL, int OK>
 __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
                                             const unsigned char* __restrict__ lds,
                                             uint16_t* __restrict__ ring) {
+  constexpr bool kWs = TL == kTabWorkspace;
   const uint32_t B = BT ? uint32_t(BT) : T.b;
   const uint32_t M = 1u << B;
   const uint32_t MASK = M - 1u;
-  const uint32_t S = GT ? M : lds_stride(WIDE);             // sym / val table stride
+  const uint32_t S = kWs ? M : 256u;                        // sym / val stride (narrow, workspace)
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t half = lane >> 5;
-  const uint32_t hs = half << 4;                            // selects this half's packed pointer
+  const uint32_t hs = half << 4;                            // selects this half's packed 16 bits
   const uint32_t l = lane & 31u;
   const uint32_t t = tile0 + 2u * (threadIdx.x >> 6) + half;
   const bool tile_ok = t < T.T;
@@ -270,7 +317,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
   }
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(T.payload, T.payload_bytes);
   const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, T.out_bytes);
-  const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.row_scales, T.rows * 4u);
+  const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 4u);
 
   // ---- per-half-wave uniform state (scalar registers)
   const uint32_t n0 = __builtin_amdgcn_readlane(n, 0), n1 = __builtin_amdgcn_readlane(n, 32);
@@ -286,15 +333,19 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
   const uint32_t kmax = max((n0 + 31u) >> 5, (n1 + 31u) >> 5);
 
   const uint32_t f0 = ((const EP_GLOBAL uint16_t*)T.freqs)[T.freq_base[0]];   // coset bit: frequency of c = 0
-  const uint32_t f1 = M - f0;
-  uint32_t f0v = f0, f1v = f1;                                // per-lane copies for selects
+  uint32_t f0v = f0, f1v = M - f0;                          // per-lane copies for the selects
   asm volatile("" : "+v"(f0v), "+v"(f1v));
-  const float scale = T.scale;
   const uint32_t kpar = T.kpar;
   const uint32_t empty = T.empty_mask;
-  const unsigned char* gtab = T.tab;
-  const uint32_t lut_bytes = GT ? (32u << B) : uint32_t(lds_lut_bytes(B, WIDE));
-  const unsigned char* tbase = GT ? gtab : lds;
+  const bool slow_rows = T.slow_rows != 0;
+  const unsigned char* tbase = kWs ? T.tab : lds;
+  const uint32_t lut_bytes = uint32_t(lut_bytes_of(TL, B));
+  // packed tables: fields 5..8 of b = 11 lie beyond the 16-bit LDS offset of
+  // the lookup instruction, so they get a second coset base
+  constexpr bool kSplit = TL == kTabPacked && (size_t(14) << BT) * 4u > 65535u;
+  // packed tables: lane i < 18 holds value constant i (see DevTensor::kvals);
+  // a lane fetches the one for its coset with ds_bpermute
+  const uint32_t kreg = TL == kTabPacked ? ((const EP_GLOBAL uint32_t*)T.kvals)[l] : 0u;
 
   // the chunk held in registers is always the one starting at word F of the half
   u32x2 pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane, 0, 0);
@@ -314,7 +365,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
     const bool active = (k * 32u + l) < n;
     const uint64_t actm = __builtin_amdgcn_ballot_w64(active);
     const uint32_t x_saved = x;
-    const float rs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
+    // Issued before the ring prefetch below: loads retire in order, so waiting
+    // for this one later does not also wait for the prefetch.
+    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
 
     // ---- ring: store the held chunk if it is useful and fits ...
     {
@@ -355,8 +408,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
     const uint32_t nlo = uint32_t(nm), nhi = uint32_t(nm >> 32);                      \
     const uint32_t clo = __builtin_popcount(nlo), chi = __builtin_popcount(nhi);      \
     /* both halves' ring pointers in one scalar: half 1 pre-corrected for the      \
-       half-0 bits that mbcnt_lo also counts; only the low 10 bits matter */        \
-    const uint32_t pk = (P0 & 0xFFFFu) | ((P1 - clo) << 16);                          \
+       half-0 bits that mbcnt_lo also counts; only the low 9 bits matter */         \
+    const u16x2 pkv = {uint16_t(P0), uint16_t(P1 - clo)};                             \
+    const uint32_t pk = __builtin_bit_cast(uint32_t, pkv);                            \
     if ((x < kL) & active) {                                                          \
       const uint32_t idx = __builtin_amdgcn_mbcnt_hi(nhi, __builtin_amdgcn_mbcnt_lo(nlo, pk >> hs)); \
       x = (x << 16) | ring[idx & (kRingWords - 1u)];                                  \
@@ -373,53 +427,96 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
     EP_RENORM();
     if (empty & 6u) empty_err |= __builtin_amdgcn_ballot_w64(active && ((empty >> (c ? 2 : 1)) & 1u));
 
-    // ---- fields z1..z7, m
-    const uint32_t lb = c ? M : 0u;                 // coset offset inside each table pair
-    // coset table base, including the table block's own offset so that the
-    // per-field offsets fit the 16-bit immediate of the LDS reads
-    uint32_t cb = c ? lut_bytes + S * 4u : lut_bytes;
-    if (!GT) asm volatile("" : "+v"(cb));
-    uint32_t sv[9];
+    // ---- fields z1..z7, m; vv[f] becomes 2 z_f + c (exact in fp32)
     float vv[9];
+    uint32_t par;
+    if (TL == kTabPacked) {
+      uint32_t ev[9];
+      uint32_t lbl = c ? (M << 2) : 0u;                  // byte offset of the coset's table
+      uint32_t lbh = lbl + (kSplit ? (8u << B) * 4u : 0u);
+      // opaque to the optimiser, so that the lookup address stays one
+      // v_and_or_b32 with the table offset folded into the LDS instruction
+      asm volatile("" : "+v"(lbl), "+v"(lbh));
 #pragma unroll
-    for (int f = 1; f <= 8; ++f) {
-      const uint32_t addr = (x & MASK) | lb;        // slot + coset * 2^b
-      uint32_t s;
-      if (GT) s = reinterpret_cast<const uint16_t*>(gtab)[(uint32_t(2 * (f - 1)) << B) + addr];
-      else if (WIDE) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr];
-      else s = lds[(uint32_t(2 * (f - 1)) << B) + addr];
-      const uint32_t eo = cb + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
-      const uint32_t e = *reinterpret_cast<const uint32_t*>(tbase + eo);
-      vv[f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
-      q = x >> B;
-      x = __umul24(e & (GT ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
-      sv[f] = GT ? s : e;
-      EP_RENORM();
+      for (int f = 1; f <= 8; ++f) {
+        const bool hi = kSplit && f >= 5;
+        const uint32_t toff = (uint32_t(2 * (f - 1) - (hi ? 8 : 0)) << B) * 4u;
+        const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << 2) & (MASK << 2)) | (hi ? lbh : lbl)) + toff);
+        q = x >> B;
+        x = __umul24(__builtin_amdgcn_ubfe(e, 11, 12), q) + (e & 0x7FFu);
+        ev[f] = e;
+        EP_RENORM();
+      }
+      // value of z_f: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 + 2 s (+1
+      // when f = 2^11), and the per-table constant turns it into 2 z + c
+      const int kaddr = c ? 4 : 0;
+#pragma unroll
+      for (int f = 1; f <= 7; ++f) {
+        const float u = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22));
+        const float kf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 8 * (f - 1), int(kreg)));
+        vv[f] = u - kf;
+      }
+      // parity of z1 + ... + z7: bit 23 of each entry is the parity of its
+      // symbol index, the constant supplies the parity of the minima
+      const uint32_t kp = uint32_t(__builtin_amdgcn_ds_bpermute(kaddr + 64, int(kreg)));
+      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+          __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
+          __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
+          ev[7] ^ kp, 0x96);
+      par = __builtin_amdgcn_ubfe(x3, 23, 1);
+      // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + c + 4 min
+      const uint32_t u8 = ((ev[8] >> 23) << 2) + ((par << 1) | (0x4B400000u | uint32_t(c)));
+      const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
+      vv[8] = __builtin_bit_cast(float, u8) - k8;
+    } else {
+      uint32_t sv[9];
+      const uint32_t lb = c ? M : 0u;                    // coset offset inside each table pair
+      // symbol tables: coset base including the block's own offset, so that
+      // the per-field LDS offsets fit the 16-bit immediate
+      uint32_t cb = c ? lut_bytes + S * 4u : lut_bytes;
+      if (TL == kTabNarrow) asm volatile("" : "+v"(cb));
+#pragma unroll
+      for (int f = 1; f <= 8; ++f) {
+        const uint32_t addr = (x & MASK) | lb;           // slot + coset * 2^b
+        uint32_t s;
+        if (kWs) s = reinterpret_cast<const uint16_t*>(tbase)[(uint32_t(2 * (f - 1)) << B) + addr];
+        else s = lds[(uint32_t(2 * (f - 1)) << B) + addr];
+        const uint32_t eo = cb + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
+        const uint32_t e = *reinterpret_cast<const uint32_t*>(tbase + eo);
+        vv[f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
+        q = x >> B;
+        x = __umul24(e & (kWs ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
+        sv[f] = kWs ? s : e;
+        EP_RENORM();
+      }
+      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(sv[1], sv[2], sv[3], 0x96),
+                                                      __builtin_amdgcn_bitop3_b32(sv[4], sv[5], sv[6], 0x96),
+                                                      sv[7], 0x96);
+      // narrow: bit 15 of the symbol entries is the parity of z; workspace:
+      // parity of the symbol indices, corrected by the parity of the minima
+      par = TL == kTabNarrow ? __builtin_amdgcn_ubfe(x3, 15, 1) : (x3 ^ (kpar >> (c ? 1 : 0))) & 1u;
+      vv[8] = vv[8] + float(par << 1);                   // the m table holds 4 m + c
     }
 #undef EP_RENORM
     x = active ? x : x_saved;
 
-    // ---- reconstruction: z8 = 2m + parity(z1 + ... + z7); the m table holds 2m + c/2
-    const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(sv[1], sv[2], sv[3], 0x96),
-                                                    __builtin_amdgcn_bitop3_b32(sv[4], sv[5], sv[6], 0x96),
-                                                    sv[7], 0x96);
-    // LDS layouts: bit 15 of the entries is the parity of z; workspace layout:
-    // parity of the symbol indices corrected by the parity of the minima
-    const uint32_t par = GT ? ((x3 ^ (kpar >> (c ? 1 : 0))) & 1u) : __builtin_amdgcn_ubfe(x3, 15, 1);
-    vv[8] = vv[8] + float(par);
-    // inactive lanes (past the end of their tile) write past the end of the
-    // output, and the hardware drops the store
+    // ---- y = (z + c/2) * g, computed as (2 z + c) * (g/2) when g/2 is exact
+    // (the row multiplier array then holds g/2; otherwise g and the slow form)
     const uint32_t ob = active ? (g + k * 32u) * out_vec_bytes(OK) : T.out_bytes;
     if (OK == kOutLattice) {
-      const i32x4 lo4 = {int(2.0f * vv[1]), int(2.0f * vv[2]), int(2.0f * vv[3]), int(2.0f * vv[4])};
-      const i32x4 hi4 = {int(2.0f * vv[5]), int(2.0f * vv[6]), int(2.0f * vv[7]), int(2.0f * vv[8])};
+      const i32x4 lo4 = {int(vv[1]), int(vv[2]), int(vv[3]), int(vv[4])};
+      const i32x4 hi4 = {int(vv[5]), int(vv[6]), int(vv[7]), int(vv[8])};
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo4), rO, ob, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi4), rO, ob + 16u, 0, 0);
     } else {
-      const float gs = __fmul_rn(scale, rs);
       float y[8];
+      if (!slow_rows) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], gs);
+        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], rv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(vv[i + 1], 0.5f), rv);
+      }
       if (OK == kOutBF16) {
         const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                          pack_bf16x2(y[6], y[7])};
@@ -464,24 +561,24 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
 }
 
 // Persistent decode kernel: block i walks a contiguous range of chunks (32 tiles
-// of one tensor each).  LDS variants stage the tensor's decode tables once per
+// of one tensor each).  LDS layouts stage the tensor's decode tables once per
 // run of chunks from the same tensor.
-template <int BT, bool GT, int OK, bool WIDE>
+template <int BT, int TL, int OK>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
                                                         const Chunk* __restrict__ chunks,
                                                         uint32_t nchunks) {
-  __shared__ __align__(16) unsigned char smem[(GT ? 0 : lds_table_bytes(BT, WIDE)) + kRingBytes];
+  constexpr size_t kTab = TL == kTabWorkspace ? 0 : table_bytes_of(TL, BT);
+  __shared__ __align__(16) unsigned char smem[kTab + kRingBytes];
   const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
   const uint32_t c0 = blockIdx.x * per;
   const uint32_t c1 = min(nchunks, c0 + per);
-  // LDS: [decode tables (LDS variants)][32 rings of kRingWords]
-  const uint32_t ring_off = GT ? 0u : uint32_t(lds_table_bytes(BT, WIDE));
-  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + ring_off) + (threadIdx.x >> 5) * kRingWords;
+  // LDS: [decode tables (LDS layouts)][32 rings of kRingWords]
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 5) * kRingWords;
   uint32_t cur = 0xFFFFFFFFu;
   for (uint32_t ci = c0; ci < c1; ++ci) {
     const Chunk ch = chunks[ci];
     const DevTensor& T = tens[ch.tensor];
-    if (!GT && ch.tensor != cur) {
+    if (TL != kTabWorkspace && ch.tensor != cur) {
       __syncthreads();
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)T.tab;
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
@@ -489,22 +586,20 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       __syncthreads();
     }
     cur = ch.tensor;
-    decode_pair<BT, GT, OK, WIDE>(T, ch.tile0, smem, ring);
+    decode_pair<BT, TL, OK>(T, ch.tile0, smem, ring);
   }
 }
 
 // ---------------------------------------------------------------- host side
-
 uint32_t choose_variant(const ep_tensor_desc& d) {
   uint32_t amax = 0;
   for (int k = 1; k < kTables; ++k) amax = std::max(amax, d.alphabet[k]);
-  if (d.prob_bits <= 11 && amax <= lds_stride(true) && lds_table_bytes(d.prob_bits, true) + kRingBytes <= kMaxLds)
-    return kVarW9 + (d.prob_bits - 9);
-  if (d.prob_bits == 12 && amax <= lds_stride(false) && lds_table_bytes(12, false) + kRingBytes <= kMaxLds)
+  if (d.prob_bits <= 11 && amax <= 512 && table_bytes_of(kTabPacked, d.prob_bits) + kRingBytes <= kMaxLds)
+    return kVarP9 + (d.prob_bits - 9);
+  if (d.prob_bits == 12 && amax <= 256 && table_bytes_of(kTabNarrow, 12) + kRingBytes <= kMaxLds)
     return kVarN12;
-  return kVarGlobal;
+  return kVarWs;
 }
-
 
 constexpr uint32_t kNumGroups = kNumVariants * kNumOutKinds;   // one launch per non-empty group
 
@@ -520,7 +615,7 @@ int out_kind_of(int dtype) {
 
 struct Layout {
   size_t tens_off, chunk_off, total;
-  std::vector<size_t> tab_off, tab_bytes;
+  std::vector<size_t> tab_off, tab_bytes, row_off;
   std::vector<uint32_t> variant, group;
   size_t nchunks;
   size_t group_chunks[kNumGroups];
@@ -542,8 +637,12 @@ int validate(const ep_tensor_desc& d, int i) {
   const uint64_t T = (nv + d.vectors_per_tile - 1) / d.vectors_per_tile;
   if (T != d.num_tiles) return bad("num_tiles != ceil(rows*cols/8 / vectors_per_tile)");
   if (d.alphabet[0] != 2 || d.min_offset[0] != 0) return bad("table 0 must be the coset bit (alphabet 2, min 0)");
-  for (int k = 1; k < kTables; ++k)
+  for (int k = 1; k < kTables; ++k) {
     if (d.alphabet[k] > (1u << d.prob_bits)) return bad("alphabet exceeds 2^prob_bits");
+    // |4 z + c| < 2^22 keeps every reconstructed value exact in fp32
+    const int64_t lo = d.min_offset[k], hi = lo + int64_t(d.alphabet[k]);
+    if (lo < -(int64_t(1) << 19) || hi > (int64_t(1) << 19)) return bad("lattice coordinates beyond +-2^19");
+  }
   if (2 * ((d.payload_words + 7) / 8 * 8) >= (uint64_t(1) << 32)) return bad("payload must be < 4 GiB");
   // 32-bit output offsets: every vector a tile's lanes can address stays below 2^32 bytes
   if ((nv + 64ull * d.vectors_per_tile + 64) * 32ull >= (uint64_t(1) << 32))
@@ -564,6 +663,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   L.nchunks = 0;
   L.tab_off.resize(n);
   L.tab_bytes.resize(n);
+  L.row_off.resize(n);
   L.variant.resize(n);
   L.group.resize(n);
   for (uint32_t v = 0; v < kNumGroups; ++v) L.group_chunks[v] = 0;
@@ -575,8 +675,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     if (ok < 0) return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": unknown output dtype");
     L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
-    L.tab_bytes[i] = L.variant[i] == kVarGlobal ? global_table_bytes(d.prob_bits)
-                                                : lds_table_bytes(d.prob_bits, L.variant[i] != kVarN12);
+    L.tab_bytes[i] = table_bytes_of(layout_of(L.variant[i]), d.prob_bits);
     const size_t nc = (d.num_tiles + kTilesPerChunk - 1) / kTilesPerChunk;
     L.nchunks += nc;
     L.group_chunks[L.group[i]] += nc;
@@ -587,13 +686,15 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   for (int i = 0; i < n; ++i) {
     L.tab_off[i] = off;
     off = align256(off + (descs[i].num_tiles ? L.tab_bytes[i] : 0));
+    L.row_off[i] = off;
+    off = align256(off + (descs[i].num_tiles ? 4 * size_t(descs[i].rows) : 0));
   }
   L.total = std::max<size_t>(off, 256);
   return EP_OK;
 }
 
 struct Group {
-  uint32_t chunk_begin, nchunks, lds, grid;
+  uint32_t chunk_begin, nchunks, grid, pad;
 };
 
 struct PlanImpl {
@@ -603,33 +704,33 @@ struct PlanImpl {
   Group groups[kNumGroups];
 };
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
-constexpr uint64_t kPlanMagic = 0x45504c414e763033ull;
+constexpr uint64_t kPlanMagic = 0x45504c414e763034ull;
 
 using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t);
 
-template <int BT, bool GT, bool WIDE>
+template <int BT, int TL>
 KernelFn kernel_for_kind(int ok) {
   switch (ok) {
-    case kOutBF16: return decode_kernel<BT, GT, kOutBF16, WIDE>;
-    case kOutFP8: return decode_kernel<BT, GT, kOutFP8, WIDE>;
-    case kOutINT8: return decode_kernel<BT, GT, kOutINT8, WIDE>;
-    default: return decode_kernel<BT, GT, kOutLattice, WIDE>;
+    case kOutBF16: return decode_kernel<BT, TL, kOutBF16>;
+    case kOutFP8: return decode_kernel<BT, TL, kOutFP8>;
+    case kOutINT8: return decode_kernel<BT, TL, kOutINT8>;
+    default: return decode_kernel<BT, TL, kOutLattice>;
   }
 }
 
 KernelFn kernel_of(uint32_t group) {
   const int ok = int(group % kNumOutKinds);
   switch (group / kNumOutKinds) {
-    case kVarW9: return kernel_for_kind<9, false, true>(ok);
-    case kVarW10: return kernel_for_kind<10, false, true>(ok);
-    case kVarW11: return kernel_for_kind<11, false, true>(ok);
-    case kVarN12: return kernel_for_kind<12, false, false>(ok);
-    default: return kernel_for_kind<0, true, true>(ok);
+    case kVarP9: return kernel_for_kind<9, kTabPacked>(ok);
+    case kVarP10: return kernel_for_kind<10, kTabPacked>(ok);
+    case kVarP11: return kernel_for_kind<11, kTabPacked>(ok);
+    case kVarN12: return kernel_for_kind<12, kTabNarrow>(ok);
+    default: return kernel_for_kind<0, kTabWorkspace>(ok);
   }
 }
 
 // Persistent grid: as many blocks as can be resident at once (at least one).
-int resident_grid(uint32_t v, uint32_t nchunks, uint32_t* grid) {
+int resident_grid(uint32_t group, uint32_t nchunks, uint32_t* grid) {
   static int cus = 0;
   hipError_t e;
   if (cus == 0) {
@@ -638,9 +739,9 @@ int resident_grid(uint32_t v, uint32_t nchunks, uint32_t* grid) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("device query: ") + hipGetErrorString(e));
   }
-  KernelFn fn = kernel_of(v);
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_of(group)),
+                                                   kBlock, 0);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
   const uint64_t g = uint64_t(std::max(per_cu, 1)) * uint64_t(std::max(cus, 1));
   *grid = uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(g, nchunks)));
@@ -693,7 +794,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   DevTensor* ht = reinterpret_cast<DevTensor*>(host.data() + L.tens_off);
   Chunk* hc = reinterpret_cast<Chunk*>(host.data() + L.chunk_off);
   char* wsb = static_cast<char*>(workspace);
-  // chunks are grouped by table placement; each group is one kernel launch
+  // chunks are grouped by (table placement, output kind); each group is one launch
   size_t group_pos[kNumGroups];
   for (size_t v = 0, acc = 0; v < kNumGroups; ++v) {
     group_pos[v] = acc;
@@ -703,7 +804,6 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   for (uint32_t v = 0; v < kNumGroups; ++v) {
     P->groups[v].chunk_begin = uint32_t(group_pos[v]);
     P->groups[v].nchunks = uint32_t(L.group_chunks[v]);
-    P->groups[v].lds = 0;
     P->groups[v].grid = 0;
     if (L.group_chunks[v]) {
       rc = resident_grid(v, uint32_t(L.group_chunks[v]), &P->groups[v].grid);
@@ -713,9 +813,8 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   for (int i = 0; i < n; ++i) {
     const ep_tensor_desc& d = descs[i];
     const int dt = dtypes[i];
-    if (dt != EP_OUT_BF16 && dt != EP_OUT_FP8_E4M3 && dt != EP_OUT_INT8 && dt != EP_OUT_LATTICE2X_I32)
-      return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": unknown output dtype");
-    const size_t align = dt == EP_OUT_BF16 || dt == EP_OUT_LATTICE2X_I32 ? 16 : 8;
+    const int ok = out_kind_of(dt);
+    const size_t align = ok == kOutBF16 || ok == kOutLattice ? 16 : 8;
     if (d.num_tiles > 0 && (!outs[i] || reinterpret_cast<uintptr_t>(outs[i]) % align != 0))
       return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": output NULL or misaligned");
     DevTensor& D = ht[i];
@@ -726,18 +825,19 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.b = d.prob_bits;
     D.rows = uint32_t(d.rows);
     D.scale = d.scale;
-    D.dtype = dt;
     D.variant = L.variant[i];
     D.tab_bytes = uint32_t(L.tab_bytes[i]);
+    D.payload_words = d.payload_words;
+    D.payload_bytes = uint32_t(2 * ((d.payload_words + 7) / 8 * 8));
+    D.out_bytes = uint32_t(D.nvec * out_vec_bytes(ok));
     D.row_scales = d.row_scales;
     D.states = d.tile_states;
     D.offsets = d.tile_offsets;
     D.payload = d.payload;
-    D.payload_words = d.payload_words;
-    D.payload_bytes = uint32_t(2 * ((d.payload_words + 7) / 8 * 8));
-    D.out_bytes = uint32_t(D.nvec * out_vec_bytes(out_kind_of(dt)));
     D.freqs = d.freqs;
     D.tab = reinterpret_cast<unsigned char*>(wsb + L.tab_off[i]);
+    D.rowv = reinterpret_cast<float*>(wsb + L.row_off[i]);
+    D.slow_rows = 0;
     D.out = outs[i];
     D.status = tile_status ? tile_status[i] : nullptr;
     uint32_t em = 0, kpar = 0;
@@ -752,6 +852,17 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       for (int f = 1; f <= 7; ++f) sum += d.min_offset[1 + 2 * (f - 1) + c];
       kpar |= uint32_t(sum & 1) << c;
     }
+    for (int t = 0; t < 32; ++t) D.kvals[t] = 0;
+    for (int t = 0; t < 16; ++t) {
+      const int64_t mn = d.min_offset[1 + t], c = t & 1;
+      // f = 2^11 (a one-symbol table at b = 11) sets bit 22 of the packed entry
+      const int64_t fb = (d.prob_bits == 11 && d.alphabet[1 + t] == 1) ? 1 : 0;
+      const int64_t kv = t < 14 ? 12582912 + fb - (2 * mn + c) : 12582912 - 4 * mn;
+      const float kf = float(kv);                   // exact: kv lies in [2^23, 2^24)
+      std::memcpy(&D.kvals[t], &kf, 4);
+    }
+    D.kvals[16] = (kpar & 1u) << 23;
+    D.kvals[17] = ((kpar >> 1) & 1u) << 23;
     D.empty_mask = em;
     D.kpar = kpar;
     for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += kTilesPerChunk)
@@ -761,8 +872,8 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   hipError_t e = hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
   if (n > 0) {
-    hipLaunchKernelGGL(build_tables_kernel, dim3(16, n), dim3(256), 0, st,
-                       reinterpret_cast<const DevTensor*>(wsb + L.tens_off));
+    hipLaunchKernelGGL(build_tables_kernel, dim3(17, n), dim3(256), 0, st,
+                       reinterpret_cast<DevTensor*>(wsb + L.tens_off));
     e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
   }
@@ -782,8 +893,8 @@ int ep_batch_launch(const ep_batch_plan* plan, void* stream) {
   for (uint32_t v = 0; v < kNumGroups; ++v) {
     const Group& G = P->groups[v];
     if (G.nchunks == 0) continue;
-    hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream),
-                       tens, chunks + G.chunk_begin, G.nchunks);
+    hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), tens,
+                       chunks + G.chunk_begin, G.nchunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   }
