@@ -31,6 +31,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "dit_weight_compression_amd", "csrc", "ep_decode.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_decode_kernel_dit_linear_set_4bpp_bf16.md")
 METRIC = "decoded Gweights/s + % HBM roofline, 4bpp→BF16, DiT linear set, 1 GPU"
 
 
@@ -114,18 +116,69 @@ def cpu_baseline(hosts, dtype: str, budget_s: float):
                       f"{dtype} by the single-threaded CPU oracle, {spent:.1f}s"}
 
 
+def kernel_source_sha256() -> str:
+    import hashlib
+
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, tensors: int):
+    """HBM bytes per decode launch from the committed counter record, or None.
+
+    The record (a rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by a plain
+    copy of known size) only counts while the kernel source it was taken on is
+    unchanged and the workload is the same.
+    """
+    try:
+        text = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        rec = json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    if rec.get("workload") != workload or rec.get("tensors") != tensors:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_linear_set_30x5_4bpp_bf16")
     ap.add_argument("--max-tensors", type=int, default=0, help="use only the first N tensors")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cache", default="", help="directory for compressed containers (reused if present)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this decoder benchmark runs on exactly one GPU; "
@@ -219,7 +272,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, len(packed)),
         },
     }
     log(f"[bench] {len(packed)} tensors, {numel / 1e9:.3f} G weights, {8 * stored / numel:.4f} bpp; "

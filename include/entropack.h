@@ -99,7 +99,9 @@ typedef struct {
   const uint16_t* freqs;              /* the 17 tables' frequencies, table k at freq_base[k] */
   uint32_t freq_base[EP_NUM_TABLES];  /* start of table k in freqs */
   uint32_t alphabet[EP_NUM_TABLES];   /* A_k <= 2^b; alphabet[0] == 2; 0 = empty table */
-  int32_t min_offset[EP_NUM_TABLES];  /* value of symbol 0 of table k (min_offset[0] == 0) */
+  int32_t min_offset[EP_NUM_TABLES];  /* value of symbol 0 of table k (min_offset[0] == 0);
+                                         -2^19 <= min_offset[k] and min_offset[k] + A_k <= 2^19,
+                                         which keeps every reconstructed 4z + c exact in fp32 */
 } ep_tensor_desc;
 
 /* Human-readable name of a status code (static string). */

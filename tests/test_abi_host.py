@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The HIP library and the host encoder library must load, export every function
+their headers declare, and reject malformed descriptors before touching the
+device (argument errors are returned synchronously, before any launch).
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dit_weight_compression_amd as ep
+from dit_weight_compression_amd import encoder
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ep_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_decoder_library_exports_every_declared_function():
+    names = _declared_functions("entropack.h")
+    assert set(names) == set(ep.EXPORTS), names
+    L = ep.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_encoder_library_exports_every_declared_function():
+    names = _declared_functions("entropack_encode.h")
+    assert set(names) == set(encoder.EXPORTS), names
+    L = encoder.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = ep.lib()
+    text = open(os.path.join(ROOT, "include", "entropack.h")).read()
+    version = int(re.search(r"#define EP_ABI_VERSION (\d+)", text).group(1))
+    assert L.ep_abi_version() == version
+    assert L.ep_status_string(ep.EP_OK) == b"EP_OK"
+    assert L.ep_status_string(ep.EP_ERR_INVALID_ARG) == b"EP_ERR_INVALID_ARG"
+    assert L.ep_status_string(ep.EP_ERR_WORKSPACE) == b"EP_ERR_WORKSPACE"
+    assert L.ep_status_string(12345) == b"EP_UNKNOWN_STATUS"
+
+
+def _desc(rows=64, cols=256, V=64, b=11, fake_ptr=0x1000):
+    d = ep.EpTensorDesc()
+    d.rows, d.cols, d.vectors_per_tile, d.prob_bits = rows, cols, V, b
+    nvec = rows * cols // 8
+    d.num_tiles = (nvec + V - 1) // V
+    d.scale = 0.5
+    for f in ("row_scales", "tile_states", "tile_offsets", "payload", "freqs"):
+        setattr(d, f, fake_ptr)
+    d.payload_words = 100
+    d.alphabet[0] = 2
+    for k in range(1, 17):
+        d.alphabet[k] = 8
+        d.min_offset[k] = -4
+        d.freq_base[k] = 2 + 8 * (k - 1)
+    return d
+
+
+def _ws_status(d, n=1):
+    L = ep.lib()
+    size = C.c_size_t(0)
+    arr = (ep.EpTensorDesc * n)(*([d] * n))
+    rc = L.ep_workspace_size(C.cast(arr, C.c_void_p), n, C.byref(size))
+    return rc, size.value, L.ep_last_error().decode()
+
+
+def test_workspace_size_of_valid_descriptors():
+    rc, size, _ = _ws_status(_desc())
+    assert rc == ep.EP_OK and size > 0 and size % 256 == 0
+    rc2, size2, _ = _ws_status(_desc(), n=3)
+    assert rc2 == ep.EP_OK and size2 > size
+    L = ep.lib()
+    zero = C.c_size_t(7)
+    assert L.ep_workspace_size(None, 0, C.byref(zero)) == ep.EP_OK and zero.value >= 0
+
+
+@pytest.mark.parametrize("mutate, needle", [
+    (lambda d: setattr(d, "cols", 12), "cols"),
+    (lambda d: setattr(d, "rows", -1), "rows"),
+    (lambda d: setattr(d, "vectors_per_tile", 16), "vectors_per_tile"),
+    (lambda d: setattr(d, "vectors_per_tile", 8000), "vectors_per_tile"),
+    (lambda d: setattr(d, "prob_bits", 8), "prob_bits"),
+    (lambda d: setattr(d, "prob_bits", 16), "prob_bits"),
+    (lambda d: setattr(d, "num_tiles", 3), "num_tiles"),
+    (lambda d: d.alphabet.__setitem__(0, 3), "coset bit"),
+    (lambda d: d.alphabet.__setitem__(5, 4096), "alphabet"),
+    (lambda d: d.min_offset.__setitem__(3, -(1 << 20)), "2^19"),
+    (lambda d: setattr(d, "payload", 0x1002), "aligned"),
+    (lambda d: setattr(d, "freqs", None), "NULL"),
+])
+def test_malformed_descriptors_are_rejected(mutate, needle):
+    d = _desc()
+    mutate(d)
+    rc, _, msg = _ws_status(d)
+    assert rc == ep.EP_ERR_INVALID_ARG, (rc, msg)
+    assert needle in msg, msg
+
+
+def test_prepare_rejects_missing_plan_and_small_workspace():
+    L = ep.lib()
+    d = _desc()
+    arr = (ep.EpTensorDesc * 1)(d)
+    dt = (C.c_int * 1)(0)
+    outs = (C.c_void_p * 1)(0x2000)
+    vp = C.c_void_p
+    assert L.ep_batch_prepare(C.cast(arr, vp), C.cast(dt, vp), C.cast(outs, vp), None, 1,
+                              None, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    plan = ep.EpBatchPlan()
+    rc = L.ep_batch_prepare(C.cast(arr, vp), C.cast(dt, vp), C.cast(outs, vp), None, 1,
+                            None, 0, None, C.byref(plan))
+    assert rc == ep.EP_ERR_WORKSPACE
+    bad = (C.c_int * 1)(7)
+    rc = L.ep_batch_prepare(C.cast(arr, vp), C.cast(bad, vp), C.cast(outs, vp), None, 1,
+                            None, 0, None, C.byref(plan))
+    assert rc == ep.EP_ERR_INVALID_ARG and b"dtype" in L.ep_last_error()
+    # a plan that prepare did not fill is refused by launch
+    assert L.ep_batch_launch(C.byref(ep.EpBatchPlan()), None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_python_binding_has_no_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(ep, "_lib", None)
+    monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        ep.lib()
