@@ -22,6 +22,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "entropack.h"
@@ -361,9 +362,12 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
     col = g - row * T.vpr;
   }
 
-  for (uint32_t k = 0; k < kmax; ++k) {
-    const bool active = (k * 32u + l) < n;
-    const uint64_t actm = __builtin_amdgcn_ballot_w64(active);
+  // One vector round.  In full rounds every lane of both halves has a vector,
+  // so the active-lane masks fold away.
+  auto round = [&](const uint32_t k, auto full) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full)::value;
+    const bool active = kFull || (k * 32u + l) < n;
+    const uint64_t actm = kFull ? ~uint64_t(0) : __builtin_amdgcn_ballot_w64(active);
     const uint32_t x_saved = x;
     // Issued before the ring prefetch below: loads retire in order, so waiting
     // for this one later does not also wait for the prefetch.
@@ -542,7 +546,11 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
         ++row;
       }
     }
-  }
+  };
+  const uint32_t kfull = min(n0, n1) >> 5;
+  uint32_t k = 0;
+  for (; k < kfull; ++k) round(k, std::true_type{});
+  for (; k < kmax; ++k) round(k, std::false_type{});
 
   // ---- end-of-tile invariants: every state back at 2^15, every word consumed
   const uint64_t bad_state = __builtin_amdgcn_ballot_w64(x != kL);
