@@ -282,11 +282,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
-// Decode the two tiles of one wave (tile0 + 2*wave + half).  BT is the
+// Decode the two tiles of one wave (tile0 + 2*wave + half, if that slot is below
+// the chunk's tile count).  BT is the
 // probability precision when known at compile time (0: read T.b), TL the
 // table layout (LDS tables start at LDS address 0), OK the output kind.
 template <int BT, int TL, int OK>
-__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
+__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, uint32_t tiles_per_chunk,
                                             const unsigned char* __restrict__ lds,
                                             uint16_t* __restrict__ ring) {
   constexpr bool kWs = TL == kTabWorkspace;
@@ -298,8 +299,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
   const uint32_t half = lane >> 5;
   const uint32_t hs = half << 4;                            // selects this half's packed 16 bits
   const uint32_t l = lane & 31u;
-  const uint32_t t = tile0 + 2u * (threadIdx.x >> 6) + half;
-  const bool tile_ok = t < T.T;
+  const uint32_t slot = 2u * (threadIdx.x >> 6) + half;   // tile of this half-wave within the chunk
+  const uint32_t t = tile0 + slot;
+  const bool tile_ok = slot < tiles_per_chunk && t < T.T;
 
   // ---- per-lane tile start
   uint32_t n = 0, x = kL, p = 0, pend = 0;
@@ -568,13 +570,14 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0,
   }
 }
 
-// Persistent decode kernel: block i walks a contiguous range of chunks (32 tiles
-// of one tensor each).  LDS layouts stage the tensor's decode tables once per
-// run of chunks from the same tensor.
+// Persistent decode kernel: block i walks a contiguous range of chunks (up to 32
+// tiles of one tensor each; half-wave s of the block takes tile s of a chunk).
+// LDS layouts stage the tensor's decode tables once per run of chunks from the
+// same tensor.
 template <int BT, int TL, int OK>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
                                                         const Chunk* __restrict__ chunks,
-                                                        uint32_t nchunks) {
+                                                        uint32_t nchunks, uint32_t tiles_per_chunk) {
   constexpr size_t kTab = TL == kTabWorkspace ? 0 : table_bytes_of(TL, BT);
   __shared__ __align__(16) unsigned char smem[kTab + kRingBytes];
   const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       __syncthreads();
     }
     cur = ch.tensor;
-    decode_pair<BT, TL, OK>(T, ch.tile0, smem, ring);
+    decode_pair<BT, TL, OK>(T, ch.tile0, tiles_per_chunk, smem, ring);
   }
 }
 
@@ -625,8 +628,8 @@ struct Layout {
   size_t tens_off, chunk_off, total;
   std::vector<size_t> tab_off, tab_bytes, row_off;
   std::vector<uint32_t> variant, group;
-  size_t nchunks;
-  size_t group_chunks[kNumGroups];
+  size_t max_chunks;                  // chunk slots for the smallest chunk (2 tiles)
+  size_t group_tiles[kNumGroups];
 };
 
 int validate(const ep_tensor_desc& d, int i) {
@@ -668,13 +671,13 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   size_t off = 0;
   L.tens_off = off;
   off = align256(off + sizeof(DevTensor) * size_t(n));
-  L.nchunks = 0;
+  L.max_chunks = 0;
   L.tab_off.resize(n);
   L.tab_bytes.resize(n);
   L.row_off.resize(n);
   L.variant.resize(n);
   L.group.resize(n);
-  for (uint32_t v = 0; v < kNumGroups; ++v) L.group_chunks[v] = 0;
+  for (uint32_t v = 0; v < kNumGroups; ++v) L.group_tiles[v] = 0;
   for (int i = 0; i < n; ++i) {
     int rc = validate(descs[i], i);
     if (rc != EP_OK) return rc;
@@ -684,13 +687,12 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
     L.tab_bytes[i] = table_bytes_of(layout_of(L.variant[i]), d.prob_bits);
-    const size_t nc = (d.num_tiles + kTilesPerChunk - 1) / kTilesPerChunk;
-    L.nchunks += nc;
-    L.group_chunks[L.group[i]] += nc;
+    L.max_chunks += (d.num_tiles + 1) / 2;
+    L.group_tiles[L.group[i]] += d.num_tiles;
   }
-  if (L.nchunks >= (size_t(1) << 31)) return fail(EP_ERR_UNSUPPORTED, "too many tiles in one call");
+  if (L.max_chunks >= (size_t(1) << 31)) return fail(EP_ERR_UNSUPPORTED, "too many tiles in one call");
   L.chunk_off = off;
-  off = align256(off + sizeof(Chunk) * L.nchunks);
+  off = align256(off + sizeof(Chunk) * L.max_chunks);
   for (int i = 0; i < n; ++i) {
     L.tab_off[i] = off;
     off = align256(off + (descs[i].num_tiles ? L.tab_bytes[i] : 0));
@@ -702,7 +704,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
 }
 
 struct Group {
-  uint32_t chunk_begin, nchunks, grid, pad;
+  uint32_t chunk_begin, nchunks, grid, tiles_per_chunk;
 };
 
 struct PlanImpl {
@@ -714,7 +716,7 @@ struct PlanImpl {
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
 constexpr uint64_t kPlanMagic = 0x45504c414e763034ull;
 
-using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t);
+using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t, uint32_t);
 
 template <int BT, int TL>
 KernelFn kernel_for_kind(int ok) {
@@ -738,7 +740,7 @@ KernelFn kernel_of(uint32_t group) {
 }
 
 // Persistent grid: as many blocks as can be resident at once (at least one).
-int resident_grid(uint32_t group, uint32_t nchunks, uint32_t* grid) {
+int resident_grid(uint32_t group, uint32_t* grid) {
   static int cus = 0;
   hipError_t e;
   if (cus == 0) {
@@ -752,8 +754,18 @@ int resident_grid(uint32_t group, uint32_t nchunks, uint32_t* grid) {
                                                    kBlock, 0);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
   const uint64_t g = uint64_t(std::max(per_cu, 1)) * uint64_t(std::max(cus, 1));
-  *grid = uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(g, nchunks)));
+  *grid = uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(g, 1u << 20)));
   return EP_OK;
+}
+
+// Tiles per chunk: full blocks (kTilesPerChunk) when there is enough work to
+// fill every resident block many times over; otherwise spread the tiles over
+// all resident blocks (even counts, one tile per half-wave), since a tile is a
+// sequential unit and a small batch is bound by the per-tile decode latency.
+uint32_t tiles_per_chunk(size_t tiles, uint32_t resident) {
+  if (tiles >= size_t(kTilesPerChunk) * resident) return kTilesPerChunk;
+  const size_t per = (tiles + 2 * size_t(resident) - 1) / (2 * size_t(resident));
+  return uint32_t(std::min<size_t>(kTilesPerChunk, std::max<size_t>(2, 2 * per)));
 }
 
 }  // namespace
@@ -802,21 +814,29 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   DevTensor* ht = reinterpret_cast<DevTensor*>(host.data() + L.tens_off);
   Chunk* hc = reinterpret_cast<Chunk*>(host.data() + L.chunk_off);
   char* wsb = static_cast<char*>(workspace);
-  // chunks are grouped by (table placement, output kind); each group is one launch
+  // chunks are grouped by (table placement, output kind); each group is one
+  // launch with its own chunk size
+  PlanImpl* P = reinterpret_cast<PlanImpl*>(plan);
+  size_t group_chunks[kNumGroups] = {};
+  for (uint32_t v = 0; v < kNumGroups; ++v) {
+    Group& G = P->groups[v];
+    G.grid = 0;
+    G.tiles_per_chunk = kTilesPerChunk;
+    if (L.group_tiles[v] == 0) continue;
+    uint32_t resident = 0;
+    rc = resident_grid(v, &resident);
+    if (rc != EP_OK) return rc;
+    G.tiles_per_chunk = tiles_per_chunk(L.group_tiles[v], resident);
+    for (int i = 0; i < n; ++i)
+      if (L.group[i] == v) group_chunks[v] += (descs[i].num_tiles + G.tiles_per_chunk - 1) / G.tiles_per_chunk;
+    G.grid = uint32_t(std::min<size_t>(resident, group_chunks[v]));
+  }
   size_t group_pos[kNumGroups];
   for (size_t v = 0, acc = 0; v < kNumGroups; ++v) {
     group_pos[v] = acc;
-    acc += L.group_chunks[v];
-  }
-  PlanImpl* P = reinterpret_cast<PlanImpl*>(plan);
-  for (uint32_t v = 0; v < kNumGroups; ++v) {
-    P->groups[v].chunk_begin = uint32_t(group_pos[v]);
-    P->groups[v].nchunks = uint32_t(L.group_chunks[v]);
-    P->groups[v].grid = 0;
-    if (L.group_chunks[v]) {
-      rc = resident_grid(v, uint32_t(L.group_chunks[v]), &P->groups[v].grid);
-      if (rc != EP_OK) return rc;
-    }
+    P->groups[v].chunk_begin = uint32_t(acc);
+    P->groups[v].nchunks = uint32_t(group_chunks[v]);
+    acc += group_chunks[v];
   }
   for (int i = 0; i < n; ++i) {
     const ep_tensor_desc& d = descs[i];
@@ -873,7 +893,8 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.kvals[17] = ((kpar >> 1) & 1u) << 23;
     D.empty_mask = em;
     D.kpar = kpar;
-    for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += kTilesPerChunk)
+    const uint32_t tpc = P->groups[L.group[i]].tiles_per_chunk;
+    for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += tpc)
       hc[group_pos[L.group[i]]++] = Chunk{uint32_t(i), t0};
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -902,7 +923,7 @@ int ep_batch_launch(const ep_batch_plan* plan, void* stream) {
     const Group& G = P->groups[v];
     if (G.nchunks == 0) continue;
     hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), tens,
-                       chunks + G.chunk_begin, G.nchunks);
+                       chunks + G.chunk_begin, G.nchunks, G.tiles_per_chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   }

@@ -146,6 +146,11 @@ def _cfg5(n: int = 300) -> List[TensorSpec]:
     return out
 
 
+def _ref_layer(target: float) -> List[TensorSpec]:
+    # the paper's reference layer shape (an FFN projection, 3840 -> 10240), one tensor
+    return [TensorSpec(f"ref_layer_{int(target)}bpp", 10240, 3840, 6, float(target))]
+
+
 WORKLOADS = {
     "w256x512_4bpp_fp32": lambda: _cfg1(512),
     "w256x512_4bpp_fp32_s4096": lambda: _cfg1(455),
@@ -154,6 +159,8 @@ WORKLOADS = {
     "w3840_6bpp": lambda: _cfg2(6),
     "w3840_7bpp": lambda: _cfg2(7),
     "w3840_8bpp": lambda: _cfg2(8),
+    "ref_layer_10240x3840_4bpp_bf16": lambda: _ref_layer(4),
+    "ref_layer_10240x3840_8bpp_bf16": lambda: _ref_layer(8),
     "dit_linear_set_30x5_4bpp_bf16": lambda: _cfg3(30),
     "llm_prefill_16x5_fp8route_5bpp": lambda: _cfg4(16),
     "mixed_300_int8route_2or8bpp": lambda: _cfg5(300),
