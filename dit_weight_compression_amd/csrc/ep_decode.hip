@@ -50,22 +50,25 @@ constexpr size_t kMaxLds = 160 * 1024;
 //             (slot - cum) | f << 11 | symbol << 23, so that the state update
 //             is one multiply-add after a single lookup; the symbol's value
 //             follows from the entry and a per-table constant (kvals).
+//   packed wide (LDS, b = 10, 11, alphabets <= 1024, f < 2^11):
+//             (slot - cum) | f << 11 | symbol << 22.
 //   narrow    (LDS, b = 12, alphabets <= 256): u8 slot -> symbol maps, then per
 //             symbol u32 f | (cum + coset*2^b) << 16 (bit 15: parity of z) and
 //             the float value 2 z + c (4 m + c for m), at stride 256.
 //   workspace (anything else): the narrow scheme with u16 slot maps and stride
 //             2^b, read from the workspace through the caches.
-enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2 };
-enum Variant : uint32_t { kVarP9 = 0, kVarP10, kVarP11, kVarN12, kVarWs, kNumVariants };
+enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2, kTabPackedWide = 3 };
+enum Variant : uint32_t { kVarP9 = 0, kVarP10, kVarP11, kVarW10, kVarW11, kVarN12, kVarWs, kNumVariants };
 
 __host__ __device__ constexpr int layout_of(uint32_t v) {
-  return v <= kVarP11 ? kTabPacked : v == kVarN12 ? kTabNarrow : kTabWorkspace;
+  return v <= kVarP11 ? kTabPacked : v <= kVarW11 ? kTabPackedWide : v == kVarN12 ? kTabNarrow : kTabWorkspace;
 }
+__host__ __device__ constexpr bool is_packed(int tl) { return tl == kTabPacked || tl == kTabPackedWide; }
 __host__ __device__ constexpr uint32_t stride_of(int tl, uint32_t b) {
   return tl == kTabNarrow ? 256u : tl == kTabWorkspace ? (1u << b) : 0u;
 }
 __host__ __device__ constexpr size_t lut_bytes_of(int tl, uint32_t b) {
-  return (size_t(16) << b) * (tl == kTabPacked ? 4 : tl == kTabNarrow ? 1 : 2);
+  return (size_t(16) << b) * (is_packed(tl) ? 4 : tl == kTabNarrow ? 1 : 2);
 }
 __host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
   return lut_bytes_of(tl, b) + 2 * size_t(16) * stride_of(tl, b) * 4;
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
   float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
   __shared__ uint32_t scan[256];
-  __shared__ uint32_t cums[512];               // packed layout: f | cum << 16 per symbol
+  __shared__ uint32_t cums[1024];              // packed layouts: f | cum << 16 per symbol
   __shared__ uint32_t carry;
-  if (tl != kTabPacked) {
+  if (!is_packed(tl)) {
     for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
       sym[i] = 0;
       val[i] = 0.0f;
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   }
   if (A == 0) {   // empty table: never used, the decoder flags the tile
     for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
-      if (tl == kTabPacked) lut32[j] = 1u << 11;   // f = 1, slot - cum = 0, symbol 0
+      if (is_packed(tl)) lut32[j] = 1u << 11;      // f = 1, slot - cum = 0, symbol 0
       else if (tl == kTabNarrow) lut8[j] = 0;
       else lut16[j] = 0;
     }
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     }
     const uint32_t cum = carry + scan[threadIdx.x] - f;
     if (i < A) {
-      if (tl == kTabPacked) {
+      if (is_packed(tl)) {
         cums[i] = (f & 0xFFFFu) | (cum << 16);
       } else {
         // the narrow layout (b = 12, f <= 4096) keeps the parity of the value z in bit 15
@@ -212,13 +215,13 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     uint32_t lo = 0, hi = A;
     while (hi - lo > 1) {
       const uint32_t mid = (lo + hi) >> 1;
-      const uint32_t cm = tl == kTabPacked ? (cums[mid] >> 16) : (sym[mid] >> 16) - (c << b);
+      const uint32_t cm = is_packed(tl) ? (cums[mid] >> 16) : (sym[mid] >> 16) - (c << b);
       if (cm <= j) lo = mid;
       else hi = mid;
     }
-    if (tl == kTabPacked) {
+    if (is_packed(tl)) {
       const uint32_t e = cums[lo];
-      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | (lo << 23);
+      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | (lo << (tl == kTabPacked ? 23 : 22));
     } else if (tl == kTabNarrow) {
       lut8[j] = uint8_t(lo);
     } else {
@@ -345,10 +348,12 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t lut_bytes = uint32_t(lut_bytes_of(TL, B));
   // packed tables: fields 5..8 of b = 11 lie beyond the 16-bit LDS offset of
   // the lookup instruction, so they get a second coset base
-  constexpr bool kSplit = TL == kTabPacked && (size_t(14) << BT) * 4u > 65535u;
+  constexpr bool kSplit = is_packed(TL) && (size_t(14) << BT) * 4u > 65535u;
+  constexpr bool kWide = TL == kTabPackedWide;
+  constexpr uint32_t kSymShift = kWide ? 22 : 23;         // symbol index position in packed entries
   // packed tables: lane i < 18 holds value constant i (see DevTensor::kvals);
   // a lane fetches the one for its coset with ds_bpermute
-  const uint32_t kreg = TL == kTabPacked ? ((const EP_GLOBAL uint32_t*)T.kvals)[l] : 0u;
+  const uint32_t kreg = is_packed(TL) ? ((const EP_GLOBAL uint32_t*)T.kvals)[l] : 0u;
 
   // the chunk held in registers is always the one starting at word F of the half
   u32x2 pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane, 0, 0);
@@ -436,7 +441,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     // ---- fields z1..z7, m; vv[f] becomes 2 z_f + c (exact in fp32)
     float vv[9];
     uint32_t par;
-    if (TL == kTabPacked) {
+    if (is_packed(TL)) {
       uint32_t ev[9];
       uint32_t lbl = c ? (M << 2) : 0u;                  // byte offset of the coset's table
       uint32_t lbh = lbl + (kSplit ? (8u << B) * 4u : 0u);
@@ -449,29 +454,32 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         const uint32_t toff = (uint32_t(2 * (f - 1) - (hi ? 8 : 0)) << B) * 4u;
         const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << 2) & (MASK << 2)) | (hi ? lbh : lbl)) + toff);
         q = x >> B;
-        x = __umul24(__builtin_amdgcn_ubfe(e, 11, 12), q) + (e & 0x7FFu);
+        x = __umul24(__builtin_amdgcn_ubfe(e, 11, kWide ? 11 : 12), q) + (e & 0x7FFu);
         ev[f] = e;
         EP_RENORM();
       }
-      // value of z_f: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 + 2 s (+1
-      // when f = 2^11), and the per-table constant turns it into 2 z + c
+      // value of z_f.  Packed: 0x4B400000 | (e >> 22) is the float
+      // 2^23 + 2^22 + 2 s (+1 when f = 2^11), and the per-table constant turns
+      // it into 2 z + c.  Wide: the same bits give 2^23 + 2^22 + s, the
+      // constant turns it into z, and an exact fma makes 2 z + c.
       const int kaddr = c ? 4 : 0;
+      const float cf = c ? 1.0f : 0.0f;
 #pragma unroll
       for (int f = 1; f <= 7; ++f) {
         const float u = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22));
         const float kf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 8 * (f - 1), int(kreg)));
-        vv[f] = u - kf;
+        vv[f] = kWide ? __builtin_fmaf(u - kf, 2.0f, cf) : u - kf;
       }
-      // parity of z1 + ... + z7: bit 23 of each entry is the parity of its
-      // symbol index, the constant supplies the parity of the minima
+      // parity of z1 + ... + z7: bit kSymShift of each entry is the parity of
+      // its symbol index, the constant supplies the parity of the minima
       const uint32_t kp = uint32_t(__builtin_amdgcn_ds_bpermute(kaddr + 64, int(kreg)));
       const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
           __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
           __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
           ev[7] ^ kp, 0x96);
-      par = __builtin_amdgcn_ubfe(x3, 23, 1);
+      par = __builtin_amdgcn_ubfe(x3, kSymShift, 1);
       // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + c + 4 min
-      const uint32_t u8 = ((ev[8] >> 23) << 2) + ((par << 1) | (0x4B400000u | uint32_t(c)));
+      const uint32_t u8 = ((ev[8] >> kSymShift) << 2) + ((par << 1) | (0x4B400000u | uint32_t(c)));
       const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
       vv[8] = __builtin_bit_cast(float, u8) - k8;
     } else {
@@ -605,8 +613,14 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
 uint32_t choose_variant(const ep_tensor_desc& d) {
   uint32_t amax = 0;
   for (int k = 1; k < kTables; ++k) amax = std::max(amax, d.alphabet[k]);
+  bool single = false;                                 // a one-symbol table (f = 2^b)
+  for (int k = 1; k < kTables; ++k) single |= d.alphabet[k] == 1;
   if (d.prob_bits <= 11 && amax <= 512 && table_bytes_of(kTabPacked, d.prob_bits) + kRingBytes <= kMaxLds)
     return kVarP9 + (d.prob_bits - 9);
+  // the wide entry holds f in 11 bits: every f < 2^11 (no one-symbol table at b = 11)
+  if ((d.prob_bits == 10 || d.prob_bits == 11) && amax <= 1024 && !(d.prob_bits == 11 && single) &&
+      table_bytes_of(kTabPackedWide, d.prob_bits) + kRingBytes <= kMaxLds)
+    return kVarW10 + (d.prob_bits - 10);
   if (d.prob_bits == 12 && amax <= 256 && table_bytes_of(kTabNarrow, 12) + kRingBytes <= kMaxLds)
     return kVarN12;
   return kVarWs;
@@ -734,6 +748,8 @@ KernelFn kernel_of(uint32_t group) {
     case kVarP9: return kernel_for_kind<9, kTabPacked>(ok);
     case kVarP10: return kernel_for_kind<10, kTabPacked>(ok);
     case kVarP11: return kernel_for_kind<11, kTabPacked>(ok);
+    case kVarW10: return kernel_for_kind<10, kTabPackedWide>(ok);
+    case kVarW11: return kernel_for_kind<11, kTabPackedWide>(ok);
     case kVarN12: return kernel_for_kind<12, kTabNarrow>(ok);
     default: return kernel_for_kind<0, kTabWorkspace>(ok);
   }
@@ -880,17 +896,19 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       for (int f = 1; f <= 7; ++f) sum += d.min_offset[1 + 2 * (f - 1) + c];
       kpar |= uint32_t(sum & 1) << c;
     }
+    const bool wide = layout_of(L.variant[i]) == kTabPackedWide;
     for (int t = 0; t < 32; ++t) D.kvals[t] = 0;
     for (int t = 0; t < 16; ++t) {
       const int64_t mn = d.min_offset[1 + t], c = t & 1;
       // f = 2^11 (a one-symbol table at b = 11) sets bit 22 of the packed entry
       const int64_t fb = (d.prob_bits == 11 && d.alphabet[1 + t] == 1) ? 1 : 0;
-      const int64_t kv = t < 14 ? 12582912 + fb - (2 * mn + c) : 12582912 - 4 * mn;
+      const int64_t kv = t >= 14 ? 12582912 - 4 * mn : wide ? 12582912 - mn : 12582912 + fb - (2 * mn + c);
       const float kf = float(kv);                   // exact: kv lies in [2^23, 2^24)
       std::memcpy(&D.kvals[t], &kf, 4);
     }
-    D.kvals[16] = (kpar & 1u) << 23;
-    D.kvals[17] = ((kpar >> 1) & 1u) << 23;
+    const uint32_t psh = wide ? 22 : 23;
+    D.kvals[16] = (kpar & 1u) << psh;
+    D.kvals[17] = ((kpar >> 1) & 1u) << psh;
     D.empty_mask = em;
     D.kpar = kpar;
     const uint32_t tpc = P->groups[L.group[i]].tiles_per_chunk;

@@ -198,3 +198,13 @@ def test_invalid_arguments_rejected():
     with pytest.raises(ep.EpError) as ei:
         ep.decode_batch([p], "bf16", workspace=small)
     assert ei.value.status == ep.EP_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("b, s, lo, hi", [(10, 0.07, 513, 1024), (11, 0.07, 513, 1024), (11, 0.05, 1025, 2048)])
+def test_wide_alphabets(b, s, lo, hi):
+    # alphabets above 512 symbols: the wide packed layout (up to 1024 symbols at
+    # b = 10, 11), and the cached global-table layout beyond it
+    W = synthgen.student_t_weights(64, 1024, 11 + b, outlier_frac=0.002).numpy()
+    ct = oracle.encode_fixed_scale(W, s, V=96, b=b)
+    assert lo <= int(ct.alphabet[1:].max()) <= hi
+    _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8"), label=f"b={b} A={ct.alphabet[1:].max()}")
