@@ -99,9 +99,10 @@ struct alignas(16) DevTensor {
   unsigned char* tab;        // workspace: decode tables in the variant's layout
   void* out;
   int32_t* status;
-  // packed layout, value constants as fp32 bit patterns, indexed by table t:
-  // t < 14: 2^23 + 2^22 + [f = 2^11] - (2 min_t + c), t = 14, 15: 2^23 + 2^22 - 4 min_t,
-  // t = 16, 17: parity of the minima of z1..z7 in coset t - 16, at bit 23
+  // packed layouts, value constants as fp32 bit patterns, indexed by table t:
+  // t < 14: 2^23 + 2^22 + [f = 2^11] - (2 min_t + c) (wide: 2^23 + 2^22 - min_t),
+  // t = 14, 15: 2^23 + 2^22 - (4 min_t + c); t = 16, 17: parity of the minima
+  // of z1..z7 in coset t - 16, at the symbol's bit position
   uint32_t kvals[32];
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
@@ -281,6 +282,11 @@ __host__ __device__ constexpr uint32_t out_vec_bytes(int ok) {
   return ok == kOutBF16 ? 16u : ok == kOutLattice ? 32u : 8u;
 }
 
+// lane mask with the lanes of half-wave 0 if h0 and those of half-wave 1 if h1
+__device__ __forceinline__ uint64_t half_mask(bool h0, bool h1) {
+  return (h0 ? 0x00000000FFFFFFFFull : 0ull) | (h1 ? 0xFFFFFFFF00000000ull : 0ull);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
@@ -322,7 +328,11 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     }
   }
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(T.payload, T.payload_bytes);
-  const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, T.out_bytes);
+  // descriptor fields used inside the round loop, read once: the output
+  // stores could alias the descriptor as far as the compiler knows
+  const uint32_t vpr = T.vpr;
+  const uint32_t out_bytes = T.out_bytes;
+  const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, out_bytes);
   const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 4u);
 
   // ---- per-half-wave uniform state (scalar registers)
@@ -360,13 +370,14 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   // A store past the end of the output (dropped by the hardware): it makes the
   // first round see the same queue of outstanding memory operations as every
   // later round (chunk, then store), so the compiler's waits stay exact.
-  __builtin_amdgcn_raw_buffer_store_b32(0u, rO, T.out_bytes, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(0u, rO, out_bytes, 0, 0);
 
   uint32_t g = t * T.V + l;                                 // < 2^32: checked on the host
-  uint32_t row = 0, col = 0;
+  uint32_t row4 = 0, col = 0;                               // row4: byte offset of the row multiplier
   if (tile_ok) {
-    row = g / T.vpr;
-    col = g - row * T.vpr;
+    const uint32_t row = g / vpr;
+    col = g - row * vpr;
+    row4 = 4u * row;
   }
 
   // One vector round.  In full rounds every lane of both halves has a vector,
@@ -378,16 +389,16 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     const uint32_t x_saved = x;
     // Issued before the ring prefetch below: loads retire in order, so waiting
     // for this one later does not also wait for the prefetch.
-    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row * 4u, 0, 0));
+    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row4, 0, 0));
 
     // ---- ring: store the held chunk if it is useful and fits ...
     {
       const bool w0 = F0 < end0 && F0 <= P0 + kRingSlack;
       const bool w1 = F1 < end1 && F1 <= P1 + kRingSlack;
-      // both halves' predicates and fill pointers packed into one scalar each;
-      // a lane extracts its half's 16 bits (tile payloads stay below 2^16 words)
-      const uint32_t wbits = uint32_t(w0) | (uint32_t(w1) << 16);
-      if (__builtin_amdgcn_ubfe(wbits, hs, 1)) {
+      // both halves' predicates as one lane mask (the branch takes it as exec);
+      // the fill pointers packed in one scalar, a lane extracts its half's 16
+      // bits (tile payloads stay below 2^16 words)
+      if (__builtin_amdgcn_inverse_ballot_w64(half_mask(w0, w1))) {
         const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
         *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = pf;
       }
@@ -400,8 +411,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
       const bool c0 = F0 < min(P0 + kRoundWords, end0);
       const bool c1 = F1 < min(P1 + kRoundWords, end1);
       if (!(c0 || c1)) break;
-      const uint32_t cbits = uint32_t(c0) | (uint32_t(c1) << 16);
-      if (__builtin_amdgcn_ubfe(cbits, hs, 1)) {
+      if (__builtin_amdgcn_inverse_ballot_w64(half_mask(c0, c1))) {
         const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * F, 0, 0);
         *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = v;
@@ -478,8 +488,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
           __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
           ev[7] ^ kp, 0x96);
       par = __builtin_amdgcn_ubfe(x3, kSymShift, 1);
-      // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + c + 4 min
-      const uint32_t u8 = ((ev[8] >> kSymShift) << 2) + ((par << 1) | (0x4B400000u | uint32_t(c)));
+      // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + (c + 4 min), the
+      // parenthesis being part of the per-table constant
+      const uint32_t u8 = ((ev[8] >> kSymShift) << 2) + ((par << 1) | 0x4B400000u);
       const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
       vv[8] = __builtin_bit_cast(float, u8) - k8;
     } else {
@@ -516,7 +527,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
 
     // ---- y = (z + c/2) * g, computed as (2 z + c) * (g/2) when g/2 is exact
     // (the row multiplier array then holds g/2; otherwise g and the slow form)
-    const uint32_t ob = active ? (g + k * 32u) * out_vec_bytes(OK) : T.out_bytes;
+    const uint32_t ob = active ? (g + k * 32u) * out_vec_bytes(OK) : out_bytes;
     if (OK == kOutLattice) {
       const i32x4 lo4 = {int(vv[1]), int(vv[2]), int(vv[3]), int(vv[4])};
       const i32x4 hi4 = {int(vv[5]), int(vv[6]), int(vv[7]), int(vv[8])};
@@ -548,12 +559,12 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
       }
     }
     col += 32u;
-    if (col >= T.vpr) {                     // rows of at least 32 vectors wrap at most once
-      col -= T.vpr;
-      ++row;
-      while (col >= T.vpr) {
-        col -= T.vpr;
-        ++row;
+    if (col >= vpr) {                       // rows of at least 32 vectors wrap at most once
+      col -= vpr;
+      row4 += 4u;
+      while (col >= vpr) {
+        col -= vpr;
+        row4 += 4u;
       }
     }
   };
@@ -902,7 +913,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       const int64_t mn = d.min_offset[1 + t], c = t & 1;
       // f = 2^11 (a one-symbol table at b = 11) sets bit 22 of the packed entry
       const int64_t fb = (d.prob_bits == 11 && d.alphabet[1 + t] == 1) ? 1 : 0;
-      const int64_t kv = t >= 14 ? 12582912 - 4 * mn : wide ? 12582912 - mn : 12582912 + fb - (2 * mn + c);
+      const int64_t kv = t >= 14 ? 12582912 - (4 * mn + c) : wide ? 12582912 - mn : 12582912 + fb - (2 * mn + c);
       const float kf = float(kv);                   // exact: kv lies in [2^23, 2^24)
       std::memcpy(&D.kvals[t], &kf, 4);
     }
