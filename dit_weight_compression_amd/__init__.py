@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libentropack_mi355x.so")
 NTABLES = 17
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE, EP_ERR_HIP = 0, -1, -2, -3, -4
-DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "lattice2x": 100}
+DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "fp32": 4, "lattice2x": 100}
 TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1, 2, 3, 4
 
 # every symbol include/entropack.h declares
@@ -54,7 +54,7 @@ class EpTensorDesc(C.Structure):
 
 
 class EpBatchPlan(C.Structure):
-    _fields_ = [("opaque", C.c_uint64 * 64)]
+    _fields_ = [("opaque", C.c_uint64 * 128)]
 
 
 _lib = None
@@ -169,7 +169,7 @@ class PackedTensor:
 def torch_dtype(name: str):
     torch = _torch()
     return {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8,
-            "lattice2x": torch.int32}[name]
+            "fp16": torch.float16, "fp32": torch.float32, "lattice2x": torch.int32}[name]
 
 
 def workspace_size(packed: Sequence[PackedTensor]) -> int:

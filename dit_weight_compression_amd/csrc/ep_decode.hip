@@ -254,7 +254,13 @@ __device__ __forceinline__ uint32_t int8_rne(float y) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));      // RNE, overflow to inf
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const float2_t f = {a, b};
@@ -276,10 +282,12 @@ constexpr uint32_t kRoundWords = 9 * 32;                 // most words one vecto
 constexpr uint32_t kRingSlack = kRingWords - kChunkWords; // a chunk fits while fill <= read + slack
 constexpr size_t kRingBytes = size_t(kTilesPerChunk) * kRingWords * sizeof(uint16_t);
 
-enum OutKind : int { kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kNumOutKinds = 4 };
+enum OutKind : int {
+  kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kOutFP16 = 4, kOutFP32 = 5, kNumOutKinds = 6
+};
 
 __host__ __device__ constexpr uint32_t out_vec_bytes(int ok) {
-  return ok == kOutBF16 ? 16u : ok == kOutLattice ? 32u : 8u;
+  return ok == kOutBF16 || ok == kOutFP16 ? 16u : ok == kOutLattice || ok == kOutFP32 ? 32u : 8u;
 }
 
 // lane mask with the lanes of half-wave 0 if h0 and those of half-wave 1 if h1
@@ -546,6 +554,15 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                          pack_bf16x2(y[6], y[7])};
         __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
+      } else if (OK == kOutFP16) {
+        const u32x4 w = {pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
+                         pack_f16x2(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
+      } else if (OK == kOutFP32) {
+        const u32x4 lo = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+        const u32x4 hi = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(lo, rO, ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, rO, ob + 16u, 0, 0);
       } else if (OK == kOutFP8) {
         const u32x2 w = {fp8_e4m3_rne(y[0]) | (fp8_e4m3_rne(y[1]) << 8) | (fp8_e4m3_rne(y[2]) << 16) |
                              (fp8_e4m3_rne(y[3]) << 24),
@@ -645,6 +662,8 @@ int out_kind_of(int dtype) {
     case EP_OUT_FP8_E4M3: return kOutFP8;
     case EP_OUT_INT8: return kOutINT8;
     case EP_OUT_LATTICE2X_I32: return kOutLattice;
+    case EP_OUT_FP16: return kOutFP16;
+    case EP_OUT_FP32: return kOutFP32;
     default: return -1;
   }
 }
@@ -749,6 +768,8 @@ KernelFn kernel_for_kind(int ok) {
     case kOutBF16: return decode_kernel<BT, TL, kOutBF16>;
     case kOutFP8: return decode_kernel<BT, TL, kOutFP8>;
     case kOutINT8: return decode_kernel<BT, TL, kOutINT8>;
+    case kOutFP16: return decode_kernel<BT, TL, kOutFP16>;
+    case kOutFP32: return decode_kernel<BT, TL, kOutFP32>;
     default: return decode_kernel<BT, TL, kOutLattice>;
   }
 }
@@ -869,7 +890,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     const ep_tensor_desc& d = descs[i];
     const int dt = dtypes[i];
     const int ok = out_kind_of(dt);
-    const size_t align = ok == kOutBF16 || ok == kOutLattice ? 16 : 8;
+    const size_t align = out_vec_bytes(ok) >= 16 ? 16 : 8;
     if (d.num_tiles > 0 && (!outs[i] || reinterpret_cast<uintptr_t>(outs[i]) % align != 0))
       return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": output NULL or misaligned");
     DevTensor& D = ht[i];

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 #define EP_NUM_TABLES 17
 #define EP_LANES 32
 
@@ -70,6 +70,8 @@ typedef enum {
   EP_OUT_BF16 = 0,           /* uint16 bit patterns, [rows, cols] */
   EP_OUT_FP8_E4M3 = 1,       /* uint8 OCP e4m3fn codes, [rows, cols] */
   EP_OUT_INT8 = 2,           /* int8 codes, [rows, cols] */
+  EP_OUT_FP16 = 3,           /* uint16 IEEE binary16 bit patterns (RNE, overflow to inf), [rows, cols] */
+  EP_OUT_FP32 = 4,           /* float32 products y = fp32(x * fp32(s * r_row)), [rows, cols] */
   EP_OUT_LATTICE2X_I32 = 100 /* int32 2*x_i (exact lattice coordinates), for tests */
 } ep_out_dtype;
 
@@ -149,7 +151,7 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
  * workspace.
  */
 typedef struct {
-  uint64_t opaque[64];
+  uint64_t opaque[128];
 } ep_batch_plan;
 
 int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const* outs,

@@ -86,6 +86,38 @@ uint8_t epo_f32_to_fp8e4m3(float yf) {
   return (uint8_t)(sign | code);
 }
 
+/* IEEE binary16, round to nearest even: the value is rounded at the quantum of
+ * its binade (2^(e-10); subnormal quantum 2^-24 below 2^-14); a result of 2^16
+ * or more overflows to infinity (largest finite 65504). */
+uint16_t epo_f32_to_f16(float yf) {
+  double y = (double)yf;
+  uint16_t sign = signbit(y) ? 0x8000u : 0u;
+  if (isnan(y)) return (uint16_t)(sign | 0x7E00u);
+  double a = fabs(y);
+  if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+  double q;
+  if (a >= ldexp(1.0, -14)) {
+    int e;
+    frexp(a, &e);                       /* floor(log2 a) = e - 1 */
+    q = ldexp(1.0, (e - 1) - 10);
+  } else {
+    q = ldexp(1.0, -24);
+  }
+  double r = rint_even(a / q) * q;
+  if (r >= 65536.0) return (uint16_t)(sign | 0x7C00u);
+  if (r == 0.0) return sign;
+  int e;
+  frexp(r, &e);
+  int E = e - 1;                        /* r = 1.m * 2^E after rounding */
+  if (E < -14) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+  uint16_t m = (uint16_t)((r / ldexp(1.0, E) - 1.0) * 1024.0);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | m);
+}
+
+void epo_f32_to_f16_batch(const float* y, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = epo_f32_to_f16(y[i]);
+}
+
 int8_t epo_f32_to_int8(float yf) {
   double r = rint_even((double)yf);
   if (r > 127.0) r = 127.0;

@@ -27,11 +27,18 @@ def _need_gpu():
 
 
 def _gpu_out_numpy(t: torch.Tensor, kind: str) -> np.ndarray:
-    if kind == "bf16":
+    # bit patterns (signed zeros and infinities compare exactly)
+    if kind in ("bf16", "fp16"):
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     if kind == "fp8":
         return t.view(torch.uint8).cpu().numpy()
+    if kind == "fp32":
+        return t.view(torch.int32).cpu().numpy().view(np.uint32)
     return t.cpu().numpy()
+
+
+def _ref_bits(ref: np.ndarray, kind: str) -> np.ndarray:
+    return ref.view(np.uint32) if kind == "fp32" else ref
 
 
 def _check_parity(ct, kinds=("bf16", "lattice2x"), label=""):
@@ -41,6 +48,7 @@ def _check_parity(ct, kinds=("bf16", "lattice2x"), label=""):
         out, st = ep.decode_tensor(p, kind, with_status=True)
         torch.cuda.synchronize()
         got = _gpu_out_numpy(out, kind)
+        ref = _ref_bits(ref, kind)
         assert np.all(st.cpu().numpy()[: ct.T] == 0), f"{label} {kind}: tile status"
         assert np.all(rst == 0)
         if not np.array_equal(got, ref):
@@ -52,7 +60,7 @@ def test_library_exports_and_version():
     L = ep.lib()
     for name in ep.EXPORTS:
         assert hasattr(L, name)
-    assert L.ep_abi_version() == 1
+    assert L.ep_abi_version() == 2
 
 
 @pytest.mark.parametrize("V", [512, 455])
@@ -72,7 +80,7 @@ def test_every_precision(b):
     W = synthgen.student_t_weights(rows, cols, 100 + b).numpy()
     s = {9: 0.5, 10: 0.25, 11: 0.1, 12: 0.05, 13: 0.02, 14: 0.01, 15: 0.004}[b]
     ct = oracle.encode_fixed_scale(W, s, V=int(rng.integers(32, 200)), b=b)
-    _check_parity(ct, label=f"b={b} {rows}x{cols} V={ct.V}")
+    _check_parity(ct, kinds=("bf16", "lattice2x", "fp16", "fp32"), label=f"b={b} {rows}x{cols} V={ct.V}")
 
 
 def test_routes_fp8_and_int8_codes():
@@ -95,6 +103,20 @@ def test_int8_and_fp8_saturation_paths():
     _check_parity(cts, kinds=("fp8",), label="fp8 subnormals")
 
 
+def test_fp16_overflow_and_subnormal_paths():
+    # products above 65520 become infinities, products below 2^-14 FP16 subnormals
+    Wb = (synthgen.student_t_weights(64, 512, 17).numpy() * 3e6).astype(np.float32)
+    ctb = oracle.encode(Wb, 6.0)
+    ref, _ = oracle.decode(ctb, "fp16")
+    assert np.any((ref & 0x7FFF) == 0x7C00)
+    _check_parity(ctb, kinds=("fp16", "fp32"), label="fp16 overflow")
+    Wt = (synthgen.student_t_weights(64, 512, 18).numpy() * 1e-4).astype(np.float32)
+    ctt = oracle.encode(Wt, 6.0)
+    ref, _ = oracle.decode(ctt, "fp16")
+    assert np.any(((ref & 0x7C00) == 0) & ((ref & 0x3FF) != 0))
+    _check_parity(ctt, kinds=("fp16", "fp32"), label="fp16 subnormals")
+
+
 def test_single_symbol_and_empty_coset_tables():
     # all-zero rows quantise to the origin: coset 1 never occurs (its tables are
     # empty) and every coordinate table holds one symbol (f = M, no renormalisation)
@@ -113,7 +135,7 @@ def test_batch_mixed_tensors_one_call():
         tgt = float(rng.choice([2.0, 4.0, 8.0]))
         route = ["direct", "fp8", "int8"][i % 3]
         cts.append(oracle.encode(W, tgt, V=int(rng.integers(32, 500)), route=route))
-        kinds.append({"direct": "bf16", "fp8": "fp8", "int8": "int8"}[route])
+        kinds.append({"direct": ["bf16", "fp16", "fp32"][i % 9 // 3], "fp8": "fp8", "int8": "int8"}[route])
     # an empty tensor in the middle of the batch
     cts.insert(3, oracle.encode(np.zeros((0, 64), np.float32), 4.0))
     kinds.insert(3, "bf16")
@@ -122,7 +144,7 @@ def test_batch_mixed_tensors_one_call():
     torch.cuda.synchronize()
     for i, (ct, kind) in enumerate(zip(cts, kinds)):
         ref, _ = oracle.decode(ct, kind)
-        assert np.array_equal(_gpu_out_numpy(outs[i], kind), ref), f"tensor {i}"
+        assert np.array_equal(_gpu_out_numpy(outs[i], kind), _ref_bits(ref, kind)), f"tensor {i}"
         assert np.all(sts[i].cpu().numpy()[: ct.T] == 0)
 
 

@@ -76,6 +76,19 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(mine, ref)
 
 
+def test_fp16_rounding_matches_numpy_ieee_cast():
+    # numpy's float32 -> float16 cast is IEEE round-to-nearest-even with
+    # overflow to infinity and gradual underflow
+    y = _f32_samples()
+    extra = np.array([65504.0, 65519.996, 65520.0, 65535.0, 7e4, -65520.0, 2.0 ** -24, 2.0 ** -25,
+                      3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11,
+                      1.0 + 3 * 2.0 ** -11, -0.0, np.inf, -np.inf], np.float32)
+    for v in (y, extra):
+        mine = oracle.f32_to_fp16(v)
+        ref = v.astype(np.float16).view(np.uint16)
+        assert np.array_equal(mine, ref)
+
+
 def test_fp8_rounding_matches_torch_after_clamp():
     y = _f32_samples()
     mine = oracle.f32_to_fp8(y)
