@@ -216,6 +216,107 @@ def calibrate_copy(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _time_ms(fn, reps: int, warmup: int = 3) -> float:
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def linear_overhead(tokens, threads: int, reps: int):
+    """Reconstruct-then-GEMM linear call against a resident BF16 weight.
+
+    The paper's reference layer shape (10240 x 3840, 4 bpp): per call the
+    compressed weight is decoded into a BF16 scratch buffer (ep_batch_launch
+    with a prepared plan, and the complete ep_decode_batch call), then
+    y = x W^T runs as a library BF16 GEMM.  Reported per token count: the
+    resident GEMM time, both compressed-call times and the relative overhead.
+    The compressed path's output is checked bit for bit against the resident
+    GEMM on the same decoded weights.
+    """
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+    from dit_weight_compression_amd import encoder
+
+    spec = synthgen.workload("ref_layer_10240x3840_4bpp_bf16")[0]
+    W = spec.weights(device="cuda:0")
+    ct = encoder.encode(W.cpu().numpy(), spec.target_bpp, threads=threads)
+    p = ep.PackedTensor.from_arrays(ct, device="cuda:0", stored_bytes=ct.stored_bytes)
+    scratch = torch.empty((p.rows, p.cols), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda:0")
+    batch = ep.BatchArgs([p], ["bf16"], [scratch], None, ws)
+    stream = torch.cuda.current_stream()
+    sp = ep.C.c_void_p(stream.cuda_stream)
+    plan = batch.prepare(sp)
+    batch.launch(plan, sp)
+    resident = scratch.clone()
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+    rows = []
+    for T in tokens:
+        x = torch.randn(T, p.cols, generator=gen, device="cuda:0").to(torch.bfloat16)
+        y_res = torch.matmul(x, resident.t())
+        batch.launch(plan, sp)
+        y_cmp = torch.matmul(x, scratch.t())
+        torch.cuda.synchronize()
+        exact = bool(torch.equal(y_res, y_cmp))
+        t_res = _time_ms(lambda: torch.matmul(x, resident.t()), reps)
+        t_launch = _time_ms(lambda: (batch.launch(plan, sp), torch.matmul(x, scratch.t())), reps)
+        t_full = _time_ms(lambda: (batch.call(sp), torch.matmul(x, scratch.t())), reps)
+        t_dec = _time_ms(lambda: batch.launch(plan, sp), reps)
+        rows.append({"tokens": T, "gemm_ms": t_res, "decode_launch_ms": t_dec,
+                     "compressed_call_ms": t_launch, "compressed_full_call_ms": t_full,
+                     "overhead": t_launch / t_res - 1.0, "overhead_full_call": t_full / t_res - 1.0,
+                     "output_bit_exact": exact})
+    print(json.dumps({"linear_call": {"layer": [p.rows, p.cols], "stored_bpp": 8.0 * ct.stored_bytes / p.numel,
+                                      "gemm": "torch.matmul bf16", "points": rows}}), flush=True)
+
+
+def tile_sweep(sizes, threads: int, reps: int):
+    """Stored bpp and decode time of the reference layer against tile size S (coordinates)."""
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+    from dit_weight_compression_amd import encoder
+
+    out = []
+    first = True
+    for name in ("ref_layer_10240x3840_4bpp_bf16", "ref_layer_10240x3840_8bpp_bf16"):
+        spec = synthgen.workload(name)[0]
+        Wn = spec.weights(device="cuda:0").cpu().numpy()
+        for S in sizes:
+            V = max(32, S // 9)
+            ct = encoder.encode(Wn, spec.target_bpp, V=V, threads=threads)
+            p = ep.PackedTensor.from_arrays(ct, device="cuda:0", stored_bytes=ct.stored_bytes)
+            o = torch.empty((p.rows, p.cols), dtype=torch.bfloat16, device="cuda:0")
+            ws = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda:0")
+            batch = ep.BatchArgs([p], ["bf16"], [o], None, ws)
+            sp = ep.C.c_void_p(torch.cuda.current_stream().cuda_stream)
+            plan = batch.prepare(sp)
+            if first:   # first use of the library and the staging paths: not timed
+                _time_ms(lambda: batch.call(sp), reps)
+                first = False
+            t_launch = _time_ms(lambda: batch.launch(plan, sp), reps)
+            t_call = _time_ms(lambda: batch.call(sp), reps)
+            out.append({"layer": name, "S": S, "V": V, "tiles": p.T, "b": p.b,
+                        "stored_bpp": 8.0 * ct.stored_bytes / p.numel,
+                        "metadata_share": (132 * p.T + 4) / ct.stored_bytes,
+                        "decode_launch_ms": t_launch, "decode_call_ms": t_call,
+                        "gweights_per_s": p.numel / (t_call / 1e3) / 1e9})
+    print(json.dumps({"tile_sweep": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,7 +330,18 @@ def main():
     ap.add_argument("--cache", default="", help="directory for compressed containers (reused if present)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--linear", default="", metavar="TOKENS",
+                    help="only measure the reconstruct-then-GEMM linear call, e.g. 256,4096,16384")
+    ap.add_argument("--tile-sweep", default="", metavar="SIZES",
+                    help="only sweep the tile size S (coordinates), e.g. 4096,8192,16384,32768")
     args = ap.parse_args()
+
+    if args.linear:
+        linear_overhead([int(t) for t in args.linear.split(",")], args.threads, max(args.steps, 1))
+        return
+    if args.tile_sweep:
+        tile_sweep([int(t) for t in args.tile_sweep.split(",")], args.threads, max(args.steps, 1))
+        return
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, max(args.steps, 1))
