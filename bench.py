@@ -80,7 +80,9 @@ def build_inputs(specs, threads: int, device: str, cache_dir: str = ""):
     if cache_dir:
         os.makedirs(cache_dir, exist_ok=True)
     for i, spec in enumerate(specs):
-        path = os.path.join(cache_dir, f"{spec.name}_{spec.seed}_{spec.target_bpp}_{spec.route}.npz") if cache_dir else ""
+        key = (f"{spec.name}_{spec.rows}x{spec.cols}_{spec.seed}_{spec.target_bpp}_{spec.route}"
+               f"_V{spec.vectors_per_tile or 0}_b{spec.prob_bits or 0}_o{spec.outlier_frac}_{int(spec.bf16)}")
+        path = os.path.join(cache_dir, key + ".npz") if cache_dir else ""
         if path and os.path.exists(path):
             ct = _load_cached(path)
         else:
