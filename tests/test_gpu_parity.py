@@ -230,3 +230,25 @@ def test_wide_alphabets(b, s, lo, hi):
     ct = oracle.encode_fixed_scale(W, s, V=96, b=b)
     assert lo <= int(ct.alphabet[1:].max()) <= hi
     _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8"), label=f"b={b} A={ct.alphabet[1:].max()}")
+
+
+@pytest.mark.parametrize("rows, cols, V", [
+    (40, 8, 32),        # one vector per row: every round wraps 32 rows
+    (33, 16, 33),       # two vectors per row, V not a multiple of 32
+    (7, 248, 61),       # 31 vectors per row
+    (1, 4096, 7200),    # V at its maximum, one row, one partial tile
+    (300, 64, 7200),    # several rows per tile at the maximum V
+])
+def test_row_wrap_and_tile_size_limits(rows, cols, V):
+    W = synthgen.student_t_weights(rows, cols, rows * 1000 + cols).numpy()
+    ct = oracle.encode_fixed_scale(W, 0.1, V=V, b=11)
+    assert ct.V == V and ct.alphabet[1:].max() > 8
+    _check_parity(ct, kinds=("bf16", "lattice2x", "int8"), label=f"{rows}x{cols} V={V}")
+
+
+def test_tensor_smaller_than_one_round():
+    # fewer vectors than lanes in a half-wave: a single partial round
+    W = synthgen.student_t_weights(2, 64, 77).numpy()
+    ct = oracle.encode_fixed_scale(W, 0.1, V=32, b=11)
+    assert ct.T == 1 and ct.rows * ct.cols // 8 < 32
+    _check_parity(ct, kinds=("bf16", "lattice2x", "fp32"), label="16 vectors")
