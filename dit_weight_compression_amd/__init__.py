@@ -25,6 +25,10 @@ TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1,
 # every symbol include/entropack.h declares
 EXPORTS = ["ep_status_string", "ep_last_error", "ep_abi_version", "ep_workspace_size",
            "ep_decode_batch", "ep_decode_tensor", "ep_batch_prepare", "ep_batch_launch"]
+# every symbol include/entropack_device_encode.h declares (same library)
+DEVICE_ENCODE_EXPORTS = ["ep_encode_device_workspace_size", "ep_encode_device",
+                         "ep_encode_device_emit"]
+ROUTES = {"direct": 0, "fp8": 1, "int8": 2}
 
 
 class EpError(RuntimeError):
@@ -84,6 +88,14 @@ def lib():
         L.ep_batch_prepare.restype = C.c_int
         L.ep_batch_launch.argtypes = [vp, vp]
         L.ep_batch_launch.restype = C.c_int
+        L.ep_encode_device_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_uint32,
+                                                      C.c_int, C.POINTER(C.c_size_t)]
+        L.ep_encode_device_workspace_size.restype = C.c_int
+        L.ep_encode_device.argtypes = [vp, C.c_int64, C.c_int64, C.c_double, C.c_uint32, C.c_uint32,
+                                       C.c_int, vp, C.c_size_t, vp, vp]
+        L.ep_encode_device.restype = C.c_int
+        L.ep_encode_device_emit.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_encode_device_emit.restype = C.c_int
         _lib = L
     return _lib
 
@@ -267,3 +279,68 @@ def decode_tensor(p: PackedTensor, dtype: str = "bf16", out=None, with_status: b
 ep_decode_tensor = decode_tensor
 ep_decode_batch = decode_batch
 ep_workspace_size = workspace_size
+
+
+# ---------------------------------------------------------------- device compressor
+def encode_device_workspace_size(rows: int, cols: int, target_bpp: float, V: int = 0,
+                                 route: str = "direct") -> int:
+    n = C.c_size_t()
+    _check(lib().ep_encode_device_workspace_size(rows, cols, float(target_bpp), V, ROUTES[route],
+                                                 C.byref(n)))
+    return n.value
+
+
+@dataclasses.dataclass
+class DeviceEncoded:
+    """Result of encode_device: the container on the device plus its header."""
+    packed: PackedTensor
+    route: str
+    route_scales: "object"   # torch float32 [rows] (FP8 / INT8 routes), else None
+    est_bpp: float
+    num_freqs: int
+
+
+def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct",
+                  workspace=None, stream=None) -> DeviceEncoded:
+    """Compress a float32 device tensor [rows, cols] with ep_encode_device.
+
+    The container matches the host compressor's byte for byte; its arrays are
+    left on W's device, ready for decode_tensor / decode_batch.
+    """
+    from .encoder import EncodedInfo
+    torch = _torch()
+    if W.dtype != torch.float32 or W.dim() != 2 or not W.is_cuda:
+        raise ValueError("W must be a 2-D float32 device tensor")
+    W = W.contiguous()
+    R, Cc = W.shape
+    dev = W.device
+    if workspace is None:
+        workspace = torch.empty(encode_device_workspace_size(R, Cc, target_bpp, V, route),
+                                dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sp = C.c_void_p(stream.cuda_stream)
+    info = EncodedInfo()
+    _check(lib().ep_encode_device(W.data_ptr() if W.numel() else None, R, Cc, float(target_bpp), V, b,
+                                  ROUTES[route], workspace.data_ptr(), workspace.numel(), sp,
+                                  C.byref(info)))
+    T, nw, nf = info.num_tiles, int(info.payload_words), info.num_freqs
+    rs = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
+    qs = torch.empty(max(R, 1), dtype=torch.float32, device=dev) if route != "direct" else None
+    st = torch.empty(max(32 * T, 1), dtype=torch.int32, device=dev)
+    off = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    # the decoder reads whole 16-byte groups: pad to a multiple of 8 words
+    pl = torch.zeros(max((nw + 7) // 8 * 8, 8), dtype=torch.int16, device=dev)
+    fr = torch.zeros(max(nf, 1), dtype=torch.int16, device=dev)
+    _check(lib().ep_encode_device_emit(workspace.data_ptr(), C.byref(info), rs.data_ptr(),
+                                       None if qs is None else qs.data_ptr(), st.data_ptr(),
+                                       off.data_ptr(), pl.data_ptr(), fr.data_ptr(), sp))
+    p = PackedTensor(R, Cc, info.vectors_per_tile, T, info.prob_bits, float(info.scale),
+                     np.array(info.alphabet, np.uint32), np.array(info.min_offset, np.int32),
+                     np.array(info.freq_base, np.uint32), rs, st, off, pl, fr,
+                     int(info.stored_bytes), nw)
+    return DeviceEncoded(p, route, qs, float(info.estimated_bpp), nf)
+
+
+ep_encode_device = encode_device
+ep_encode_device_workspace_size = encode_device_workspace_size

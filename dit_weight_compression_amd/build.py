@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libentropack_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", "ep_decode.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "ep_decode.hip"), os.path.join(HERE, "csrc", "ep_encode_gpu.hip")]
 ENC_LIB_PATH = os.path.join(HERE, "libentropack_encode.so")
 ENC_SOURCES = [os.path.join(HERE, "csrc", "ep_encode.cpp")]
 ENC_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",

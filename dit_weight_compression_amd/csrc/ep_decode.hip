@@ -818,6 +818,11 @@ uint32_t tiles_per_chunk(size_t tiles, uint32_t resident) {
 
 }  // namespace
 
+// Lets the device compressor (ep_encode_gpu.hip) report through ep_last_error.
+__attribute__((visibility("hidden"))) int ep_record_error(int code, const std::string& msg) {
+  return fail(code, msg);
+}
+
 extern "C" {
 
 const char* ep_status_string(int s) {

@@ -32,6 +32,7 @@
 
 #include "entropack.h"
 #include "entropack_encode.h"
+#include "ep_encode_common.h"
 
 struct ep_encoded {
   ep_encoded_info info;
@@ -42,9 +43,11 @@ struct ep_encoded {
 
 namespace {
 
-constexpr int kTables = 17;
-constexpr int kFields = 9;
-constexpr uint32_t kStateLow = 1u << 15;
+using ep_common::kFields;
+using ep_common::kStateLow;
+using ep_common::kTables;
+using ep_common::normalize_table;
+using ep_common::table_of;
 
 // ------------------------------------------------------------------ threads
 void parallel_for(int threads, int64_t n, const std::function<void(int64_t, int64_t)>& body) {
@@ -120,8 +123,6 @@ inline void point_twice(const int32_t* fl, int64_t* x2) {
   x2[7] = 2 * z8 + c;
 }
 
-inline int table_of(int f, int c) { return f == 0 ? 0 : 1 + 2 * (f - 1) + c; }
-
 // ------------------------------------------------------------------ route pre-cast
 uint8_t fp8_e4m3_code(float y) {
   // OCP e4m3fn: clamp to +-448, round to nearest even at the format's quantum.
@@ -175,42 +176,6 @@ void route_precast(const float* W, int64_t rows, int64_t cols, int route, float*
 }
 
 // ------------------------------------------------------------------ tables
-int normalize_table(const uint64_t* counts, uint32_t A, uint32_t b, uint16_t* out) {
-  const uint64_t M = uint64_t(1) << b;
-  uint64_t N = 0, distinct = 0;
-  for (uint32_t i = 0; i < A; ++i) {
-    N += counts[i];
-    distinct += counts[i] != 0;
-  }
-  std::fill(out, out + A, uint16_t(0));
-  if (N == 0) return 0;
-  if (distinct > M) return -1;
-  std::vector<uint32_t> f(A);
-  uint64_t sum = 0;
-  for (uint32_t i = 0; i < A; ++i) {
-    f[i] = counts[i] ? uint32_t(std::max<uint64_t>(1, counts[i] * M / N)) : 0u;
-    sum += f[i];
-  }
-  if (sum < M) {
-    uint32_t top = 0;
-    for (uint32_t i = 1; i < A; ++i)
-      if (counts[i] > counts[top]) top = i;
-    f[top] += uint32_t(M - sum);
-  } else if (sum > M) {
-    std::vector<uint32_t> big;   // indices still above one, ascending
-    for (uint32_t i = 0; i < A; ++i)
-      if (f[i] > 1) big.push_back(i);
-    for (; sum > M; --sum) {
-      size_t best = 0;
-      for (size_t j = 1; j < big.size(); ++j)
-        if (f[big[j]] > f[big[best]]) best = j;
-      if (--f[big[best]] == 1) big.erase(big.begin() + long(best));
-    }
-  }
-  for (uint32_t i = 0; i < A; ++i) out[i] = uint16_t(f[i]);
-  return 0;
-}
-
 struct TableStats {
   int32_t minv[kTables];
   uint32_t A[kTables];
@@ -273,15 +238,6 @@ void table_stats(const int32_t* fields, int64_t nvec, int threads, TableStats& t
   }
 }
 
-uint64_t stored_bytes(int64_t rows, uint64_t T, uint64_t words, const uint32_t* A, int route) {
-  uint64_t bytes = 32 + 4;                          // header, coset-bit table
-  for (int k = 1; k < kTables; ++k) bytes += 6 + 2ull * A[k];
-  bytes += 4ull * uint64_t(rows);                   // row scales
-  if (route != EP_ROUTE_DIRECT) bytes += 4ull * uint64_t(rows);
-  bytes += 132ull * T + 4 + 2ull * words;           // tile metadata, final offset, payload
-  return bytes;
-}
-
 // ------------------------------------------------------------------ encoder state
 struct Job {
   const float* Wq;
@@ -311,30 +267,6 @@ void quantize_rows(const Job& J, const int64_t* idx, int64_t nrows, double s, in
   });
 }
 
-uint64_t splitmix64_next(uint64_t& st) {
-  uint64_t z = (st += 0x9E3779B97F4A7C15ull);
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-std::vector<int64_t> sample_rows(int64_t rows, int64_t cols) {
-  const int64_t per_row = cols / 8;
-  int64_t want = per_row > 0 ? ((int64_t(1) << 18) + per_row - 1) / per_row : rows;
-  want = std::max<int64_t>(1, std::min(want, rows));
-  std::vector<int64_t> perm(size_t(std::max<int64_t>(rows, 1)));
-  for (int64_t i = 0; i < rows; ++i) perm[size_t(i)] = i;
-  uint64_t st = (uint64_t(rows) << 32) + uint64_t(cols);
-  for (int64_t i = 0; i < want && i < rows; ++i) {
-    const uint64_t j = uint64_t(i) + splitmix64_next(st) % uint64_t(rows - i);
-    std::swap(perm[size_t(i)], perm[size_t(j)]);
-  }
-  if (rows == 0) return {};
-  perm.resize(size_t(want));
-  std::sort(perm.begin(), perm.end());
-  return perm;
-}
-
 double estimate_bpp(const Job& J, double s, uint32_t b) {
   const int64_t ns = int64_t(J.sample.size());
   const int64_t nvec_s = ns * J.per_row;
@@ -343,29 +275,11 @@ double estimate_bpp(const Job& J, double s, uint32_t b) {
   quantize_rows(J, J.sample.data(), ns, s, fields.data());
   TableStats ts;
   table_stats(fields.data(), nvec_s, J.threads, ts);
-  double bits = 0.0;
-  std::vector<uint16_t> f;
-  for (int k = 0; k < kTables; ++k) {
-    if (ts.A[k] == 0) continue;
-    f.assign(ts.A[k], 0);
-    if (normalize_table(ts.counts[k].data(), ts.A[k], b, f.data()) != 0) return INFINITY;
-    for (uint32_t i = 0; i < ts.A[k]; ++i)
-      if (ts.counts[k][i]) bits += double(ts.counts[k][i]) * (double(b) - std::log2(double(f[i])));
-  }
-  const uint64_t T = (uint64_t(J.nvec) + J.V - 1) / J.V;
-  const double payload = bits * (double(J.nvec) / double(nvec_s)) / 8.0;
-  const double side = double(stored_bytes(J.rows, T, 0, ts.A, J.route));
-  return 8.0 * (payload + side) / (double(J.rows) * double(J.cols));
-}
-
-double search_scale(const Job& J, double target, uint32_t b) {
-  double lo = 1e-3, hi = 8.0;
-  for (int it = 0; it < 12; ++it) {
-    const double s = std::sqrt(lo * hi);
-    if (estimate_bpp(J, s, b) > target) lo = s;
-    else hi = s;
-  }
-  return std::sqrt(lo * hi);
+  const uint64_t* counts[kTables];
+  for (int k = 0; k < kTables; ++k) counts[k] = ts.counts[k].data();
+  const double bits = ep_common::sample_bits(counts, ts.A, b);
+  return ep_common::estimate_from_bits(bits, nvec_s, J.rows, J.cols, J.V, ts.A,
+                                       J.route != EP_ROUTE_DIRECT);
 }
 
 uint32_t max_coordinate_alphabet(const int32_t* fields, int64_t nvec, int threads) {
@@ -494,7 +408,7 @@ int finish(Job& J, float s, uint32_t b, const std::vector<int32_t>& fields, ep_e
                 E->payload.begin() + E->offsets[size_t(t)]);
   });
   I.payload_words = pos;
-  I.stored_bytes = stored_bytes(J.rows, T, pos, I.alphabet, J.route);
+  I.stored_bytes = ep_common::stored_bytes(J.rows, T, pos, I.alphabet, J.route != EP_ROUTE_DIRECT);
   return EP_OK;
 }
 
@@ -511,12 +425,9 @@ int ep_encode_host(const float* W, int64_t rows, int64_t cols, double target_bpp
   if (route < EP_ROUTE_DIRECT || route > EP_ROUTE_INT8) return EP_ERR_INVALID_ARG;
   if (uint64_t(rows) * uint64_t(cols) / 8u > 0xFFFFFFFFull) return EP_ERR_INVALID_ARG;
   uint32_t V = vectors_per_tile;
-  if (V == 0) {
-    const uint32_t S = target_bpp >= 8.0 ? 4096 : target_bpp >= 7.0 ? 8192 : target_bpp >= 4.0 ? 16384 : 32768;
-    V = std::max<uint32_t>(32, S / kFields);
-  }
+  if (V == 0) V = ep_common::default_vectors_per_tile(target_bpp);
   if (V < 32) return EP_ERR_INVALID_ARG;
-  uint32_t b = prob_bits ? prob_bits : (target_bpp <= 7.0 ? 11u : 12u);
+  uint32_t b = prob_bits ? prob_bits : ep_common::default_prob_bits(target_bpp);
   if (b < 9 || b > 15) return EP_ERR_INVALID_ARG;
   if (threads <= 0) threads = int(std::max(1u, std::thread::hardware_concurrency()));
 
@@ -554,12 +465,12 @@ int ep_encode_host(const float* W, int64_t rows, int64_t cols, double target_bpp
       J.norms[size_t(r)] = std::sqrt(acc / double(cols));
     }
   });
-  J.sample = sample_rows(rows, cols);
+  J.sample = ep_common::sample_rows(rows, cols);
 
   std::vector<int32_t> fields(size_t(std::max<int64_t>(J.nvec, 1)) * kFields);
   float s = 1.0f;
   for (;;) {
-    const double sd = search_scale(J, target_bpp, b);
+    const double sd = ep_common::search_scale(target_bpp, [&](double sc) { return estimate_bpp(J, sc, b); });
     E->info.estimated_bpp = estimate_bpp(J, sd, b);
     s = float(sd);
     quantize_rows(J, nullptr, rows, double(s), fields.data());
@@ -570,7 +481,7 @@ int ep_encode_host(const float* W, int64_t rows, int64_t cols, double target_bpp
       continue;
     }
     while (amax > (1u << b)) {
-      s = float(1.05 * double(s) * double(amax) / double(1u << b));
+      s = ep_common::coarsen_scale(s, amax, b);
       quantize_rows(J, nullptr, rows, double(s), fields.data());
       amax = max_coordinate_alphabet(fields.data(), J.nvec, threads);
     }

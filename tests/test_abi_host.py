@@ -133,3 +133,53 @@ def test_python_binding_has_no_fallback_when_library_missing(monkeypatch, tmp_pa
     monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         ep.lib()
+
+
+def test_device_encoder_exports_every_declared_function():
+    names = _declared_functions("entropack_device_encode.h")
+    assert set(names) == set(ep.DEVICE_ENCODE_EXPORTS), names
+    L = ep.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_device_encoder_workspace_size_and_argument_errors():
+    import ctypes as C
+    from dit_weight_compression_amd import encoder as enc
+    L = ep.lib()
+    n = C.c_size_t()
+    bad = [(-1, 64, 4.0, 0, 0), (4, 60, 4.0, 0, 0), (4, 0, 4.0, 0, 0), (4, 64, 4.0, 31, 0),
+           (4, 64, 4.0, 0, 3), (4, 64, 0.0, 0, 0), (4, 64, float("nan"), 0, 0)]
+    for rows, cols, tgt, V, route in bad:
+        assert L.ep_encode_device_workspace_size(rows, cols, tgt, V, route, C.byref(n)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device_workspace_size(4, 64, 4.0, 0, 0, None) == ep.EP_ERR_INVALID_ARG
+    # the per-weight arrays dominate: 36 B of fields per vector, 18 B of word scratch per tiled vector
+    sizes = {}
+    for rows, route in ((1000, 0), (2000, 0), (2000, 1)):
+        assert L.ep_encode_device_workspace_size(rows, 1024, 4.0, 0, route, C.byref(n)) == ep.EP_OK
+        sizes[rows, route] = n.value
+        nvec = rows * 1024 // 8
+        V = 16384 // 9
+        T = -(-nvec // V)
+        assert n.value >= 36 * nvec + 18 * T * V + (4 * rows * 1024 if route else 0)
+    assert sizes[2000, 0] > sizes[1000, 0] and sizes[2000, 1] > sizes[2000, 0]
+    # argument checks happen on the host, before any device call
+    info = enc.EncodedInfo()
+    fake = C.c_void_p(1 << 40)
+    ws_need = ep.encode_device_workspace_size(8, 64, 4.0)
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, fake, ws_need, None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(None, 8, 64, 4.0, 0, 0, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(C.c_void_p((1 << 40) + 4), 8, 64, 4.0, 0, 0, 0, fake, ws_need, None,
+                              C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 8, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 16, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, fake, ws_need - 1, None,
+                              C.byref(info)) == ep.EP_ERR_WORKSPACE
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, None, ws_need, None, C.byref(info)) == ep.EP_ERR_WORKSPACE
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, C.c_void_p((1 << 40) + 128), ws_need, None,
+                              C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert b"aligned" in L.ep_last_error()
+    # emit rejects a header that does not describe an encoded tensor
+    info.rows, info.cols, info.vectors_per_tile, info.num_tiles = 8, 64, 32, 99
+    assert L.ep_encode_device_emit(fake, C.byref(info), None, None, None, None, None, None,
+                                   None) == ep.EP_ERR_INVALID_ARG
