@@ -6,8 +6,10 @@ out 3840->3840, FFN up 3840->10240, gate 3840->10240, down 10240->3840},
 150 tensors, 5,308,416,000 weights -- compressed at a 4 bpp target and decoded
 to BF16 by one ep_decode_batch call per step.  Weights are seeded synthetic
 Student-t tensors (nu = 5, per-row lognormal scales) rounded to BF16, drawn on
-the GPU and compressed by the host encoder before timing; the compressed
-streams and the outputs are resident in HBM when the timed region starts.
+the GPU and compressed there by the device compressor before timing (its
+containers are byte-identical to the host compressor's, which --host-encoder
+selects); the compressed streams and the outputs are resident in HBM when the
+timed region starts.
 
 A step is one complete ep_decode_batch call (schedule upload, decode-table
 build, fused decode kernel).  HIP events on the launch stream bracket every
@@ -16,7 +18,7 @@ roofline figure: algorithmic bytes = stored bytes (payload, tile metadata,
 tables, row scales, headers) + output bytes, against 8 TB/s.
 
 The CPU baseline times the CPU oracle decoding a bounded sample of the same
-containers on this host (one thread).
+containers on this host, on one thread and on --threads threads.
 """
 from __future__ import annotations
 
@@ -68,8 +70,42 @@ def _save_cached(path, ct):
     os.replace(tmp, path)
 
 
-def build_inputs(specs, threads: int, device: str, cache_dir: str = ""):
-    """Draw, compress and upload every tensor (optionally via an on-disk container cache)."""
+class DeviceHosts:
+    """Host copies of device-compressed containers, made on first use (CPU baseline only)."""
+
+    def __init__(self, results):
+        self.results = results
+
+    def __len__(self):
+        return len(self.results)
+
+    def __iter__(self):
+        import numpy as np
+
+        from dit_weight_compression_amd import encoder
+
+        for d in self.results:
+            p = d.packed
+            R, T = p.rows, p.T
+            yield encoder.HostContainer(
+                R, p.cols, p.V, T, p.b, p.s, d.route, d.est_bpp, p.stored_bytes,
+                p.row_scales.cpu().numpy()[:R],
+                None if d.route_scales is None else d.route_scales.cpu().numpy()[:R],
+                p.states.cpu().numpy().view(np.uint32)[: 32 * T].copy(),
+                p.offsets.cpu().numpy().view(np.uint32)[: T + 1].copy(),
+                p.payload.cpu().numpy().view(np.uint16)[: p.nwords].copy(),
+                p.freqs.cpu().numpy().view(np.uint16)[: d.num_freqs].copy(),
+                p.alphabet, p.minval, p.freq_base)
+
+
+def build_inputs(specs, threads: int, device: str, cache_dir: str = "", host_encoder: bool = False):
+    """Draw and compress every tensor; the containers stay on the device.
+
+    By default the device compressor (ep_encode_device) compresses each tensor
+    where it was drawn; its containers are byte-identical to the host
+    compressor's.  With host_encoder the host compressor runs instead
+    (optionally through an on-disk container cache).
+    """
     import torch
 
     import dit_weight_compression_amd as ep
@@ -77,6 +113,23 @@ def build_inputs(specs, threads: int, device: str, cache_dir: str = ""):
 
     packed, hosts = [], []
     t0 = time.time()
+    if not host_encoder:
+        need = max(ep.encode_device_workspace_size(s.rows, s.cols, s.target_bpp, s.vectors_per_tile or 0, s.route)
+                   for s in specs)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        results = []
+        for i, spec in enumerate(specs):
+            W = spec.weights(device=device)
+            d = ep.encode_device(W, spec.target_bpp, V=spec.vectors_per_tile or 0, b=spec.prob_bits or 0,
+                                 route=spec.route, workspace=ws)
+            del W
+            results.append(d)
+            packed.append(d.packed)
+            if (i + 1) % 25 == 0 or i + 1 == len(specs):
+                log(f"[bench] device-compressed {i + 1}/{len(specs)} tensors ({time.time() - t0:.1f}s)")
+        del ws
+        torch.cuda.synchronize()
+        return packed, DeviceHosts(results)
     if cache_dir:
         os.makedirs(cache_dir, exist_ok=True)
     for i, spec in enumerate(specs):
@@ -319,6 +372,58 @@ def tile_sweep(sizes, threads: int, reps: int):
     print(json.dumps({"tile_sweep": out}), flush=True)
 
 
+def encode_timing(threads: int, reps: int):
+    """Device compressor (ep_encode_device + emit) per layer, beside the host compressor.
+
+    Layers: the reference layer 10240 x 3840 at 4 and 8 bpp, and the DiT
+    block's QKV (11520 x 3840) and down (3840 x 10240) shapes at 4 bpp.  The
+    device call synchronises internally (the scale search reads its sampled
+    counts back), so it is timed by the host clock around complete calls with
+    the input already resident.  Each layer's device container is checked
+    byte for byte against the host compressor's.
+    """
+    import time
+
+    import numpy as np
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+    from dit_weight_compression_amd import encoder
+
+    layers = [("ref_layer_10240x3840", 10240, 3840, 6, 4.0), ("ref_layer_10240x3840", 10240, 3840, 6, 8.0),
+              ("dit_qkv_11520x3840", 11520, 3840, 3000, 4.0), ("dit_down_3840x10240", 3840, 10240, 3004, 4.0)]
+    out = []
+    for name, R, Cc, seed, target in layers:
+        Wt = synthgen.student_t_weights(R, Cc, seed, bf16=True)
+        Wn = Wt.numpy()
+        Wd = Wt.to("cuda:0")
+        ws = torch.empty(ep.encode_device_workspace_size(R, Cc, target), dtype=torch.uint8, device="cuda:0")
+        d = ep.encode_device(Wd, target, workspace=ws)   # warm-up (first launches, allocator)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            d = ep.encode_device(Wd, target, workspace=ws)
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+        t0 = time.perf_counter()
+        h = encoder.encode(Wn, target, threads=threads)
+        t_host = (time.perf_counter() - t0) * 1e3
+        p = d.packed
+        same = (p.b == h.b and np.float32(p.s).tobytes() == np.float32(h.s).tobytes()
+                and p.row_scales.cpu().numpy()[:R].tobytes() == h.row_scales.tobytes()
+                and p.states.cpu().numpy().view(np.uint32).tobytes() == h.states.tobytes()
+                and p.payload.cpu().numpy().view(np.uint16)[: p.nwords].tobytes() == h.payload.tobytes()
+                and p.offsets.cpu().numpy().view(np.uint32).tobytes() == h.offsets.tobytes())
+        out.append({"layer": name, "shape": [R, Cc], "target_bpp": target, "b": p.b, "tiles": p.T,
+                    "stored_bpp": 8.0 * p.stored_bytes / p.numel,
+                    "device_encode_ms_min": min(times), "device_encode_ms_median": float(np.median(times)),
+                    "host_encode_ms": t_host, "host_threads": threads, "identical_to_host": bool(same)})
+        log(json.dumps(out[-1]))
+    print(json.dumps({"encode": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,14 +434,23 @@ def main():
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cache", default="", help="directory for compressed containers (reused if present)")
+    ap.add_argument("--host-encoder", action="store_true",
+                    help="compress the inputs with the host compressor instead of the device compressor")
+    ap.add_argument("--cache", default="",
+                    help="with --host-encoder: directory for compressed containers (reused if present)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--linear", default="", metavar="TOKENS",
                     help="only measure the reconstruct-then-GEMM linear call, e.g. 256,4096,16384")
     ap.add_argument("--tile-sweep", default="", metavar="SIZES",
                     help="only sweep the tile size S (coordinates), e.g. 4096,8192,16384,32768")
+    ap.add_argument("--encode", action="store_true",
+                    help="only time the device compressor per layer beside the host compressor")
     args = ap.parse_args()
+
+    if args.encode:
+        encode_timing(args.threads, max(args.steps, 1))
+        return
 
     if args.linear:
         linear_overhead([int(t) for t in args.linear.split(",")], args.threads, max(args.steps, 1))
@@ -370,7 +484,7 @@ def main():
         specs = specs[: args.max_tensors]
     dtypes = [s.out_dtype for s in specs]
 
-    packed, hosts = build_inputs(specs, args.threads, device, args.cache)
+    packed, hosts = build_inputs(specs, args.threads, device, args.cache, args.host_encoder)
     numel = sum(p.numel for p in packed)
     stored = sum(p.stored_bytes for p in packed)
     out_bytes = sum(p.numel * {"bf16": 2, "fp8": 1, "int8": 1}[d] for p, d in zip(packed, dtypes))

@@ -66,14 +66,22 @@ inline int normalize_table(const uint64_t* counts, uint32_t A, uint32_t b, uint1
       if (counts[i] > counts[top]) top = i;
     f[top] += uint32_t(M - sum);
   } else if (sum > M) {
-    std::vector<uint32_t> big;   // indices still above one, ascending
+    // max-heap of (f, -index) over the frequencies above one: the top is the
+    // largest frequency, lowest index first, exactly the unit a linear scan
+    // for the first maximum would take
+    std::vector<uint64_t> heap;
     for (uint32_t i = 0; i < A; ++i)
-      if (f[i] > 1) big.push_back(i);
+      if (f[i] > 1) heap.push_back((uint64_t(f[i]) << 32) | uint64_t(~i));
+    std::make_heap(heap.begin(), heap.end());
     for (; sum > M; --sum) {
-      size_t best = 0;
-      for (size_t j = 1; j < big.size(); ++j)
-        if (f[big[j]] > f[big[best]]) best = j;
-      if (--f[big[best]] == 1) big.erase(big.begin() + long(best));
+      std::pop_heap(heap.begin(), heap.end());
+      const uint32_t i = ~uint32_t(heap.back());
+      if (--f[i] == 1) {
+        heap.pop_back();
+      } else {
+        heap.back() = (uint64_t(f[i]) << 32) | uint64_t(~i);
+        std::push_heap(heap.begin(), heap.end());
+      }
     }
   }
   for (uint32_t i = 0; i < A; ++i) out[i] = uint16_t(f[i]);
@@ -125,12 +133,17 @@ inline std::vector<int64_t> sample_rows(int64_t rows, int64_t cols) {
 inline double sample_bits(const uint64_t* const* counts, const uint32_t* A, uint32_t b) {
   double bits = 0.0;
   std::vector<uint16_t> f;
+  std::vector<double> cost((size_t(1) << b) + 1, -1.0);   // b - log2(f), filled on first use
   for (int k = 0; k < kTables; ++k) {
     if (A[k] == 0) continue;
     f.assign(A[k], 0);
     if (normalize_table(counts[k], A[k], b, f.data()) != 0) return INFINITY;
     for (uint32_t i = 0; i < A[k]; ++i)
-      if (counts[k][i]) bits += double(counts[k][i]) * (double(b) - std::log2(double(f[i])));
+      if (counts[k][i]) {
+        double& c = cost[f[i]];
+        if (c < 0.0) c = double(b) - std::log2(double(f[i]));
+        bits += double(counts[k][i]) * c;
+      }
   }
   return bits;
 }

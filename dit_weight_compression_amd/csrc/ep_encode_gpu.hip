@@ -51,9 +51,9 @@ using ep_common::kFields;
 using ep_common::kStateLow;
 using ep_common::kTables;
 
-constexpr int kLdsBins = 16384;        // LDS-privatised histogram capacity (64 KB)
+constexpr int kHistBins = 32768;       // LDS-privatised histogram capacity (128 KB)
 constexpr int kRowBlock = 64;          // rows per block in the per-row passes
-constexpr int kRowChunk = 64;          // columns staged per step in the per-row passes
+constexpr int kRowChunk = 128;         // columns staged per step in the per-row passes
 
 struct HipFailure {
   int code;
@@ -237,106 +237,151 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   }
 }
 
-// Symbol counts of the 17 tables over the first nq vectors: counts[base[k] +
-// value - min[k]].  Small alphabets count in LDS first.
-__global__ __launch_bounds__(256) void histogram_kernel(const int32_t* __restrict__ fields, uint64_t stride,
-                                                       uint64_t nq, TableArgs ta, uint32_t nbins,
-                                                       uint32_t* __restrict__ counts) {
-  __shared__ uint32_t h[kLdsBins];
-  const bool lds = nbins <= uint32_t(kLdsBins);
+// Symbol counts over the first nq vectors of the bins [lo, hi) of the 17
+// tables' concatenated histograms (counts[base[k] + value - min[k]]); fmask
+// names the fields whose tables meet that range.  With lds, the block counts
+// privately first (hi - lo <= kHistBins); otherwise it adds to global memory
+// directly (one very wide table).
+__global__ __launch_bounds__(1024) void histogram_kernel(const int32_t* __restrict__ fields, uint64_t stride,
+                                                        uint64_t nq, TableArgs ta, uint32_t lo, uint32_t hi,
+                                                        uint32_t fmask, int lds, uint32_t* __restrict__ counts) {
+  __shared__ uint32_t h[kHistBins];
+  const uint32_t nb = hi - lo;
   if (lds) {
-    for (uint32_t i = threadIdx.x; i < nbins; i += blockDim.x) h[i] = 0;
+    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0;
     __syncthreads();
   }
   for (uint64_t g = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; g < nq;
        g += uint64_t(gridDim.x) * blockDim.x) {
     const int c = fields[g];
-    uint32_t bins[kFields];
-    bins[0] = ta.base[0] + uint32_t(c);
-#pragma unroll
-    for (int f = 1; f < kFields; ++f) {
-      const int k0 = 1 + 2 * (f - 1);
-      const int32_t mn = sel(c, ta.minv[k0], ta.minv[k0 + 1]);
-      const uint32_t bs = uint32_t(sel(c, int32_t(ta.base[k0]), int32_t(ta.base[k0 + 1])));
-      bins[f] = bs + uint32_t(fields[uint64_t(f) * stride + g] - mn);
-    }
 #pragma unroll
     for (int f = 0; f < kFields; ++f) {
-      if (lds) atomicAdd(&h[bins[f]], 1u);
-      else atomicAdd(&counts[bins[f]], 1u);
+      if (!((fmask >> f) & 1u)) continue;
+      uint32_t bin;
+      if (f == 0) {
+        bin = ta.base[0] + uint32_t(c);
+      } else {
+        const int k0 = 1 + 2 * (f - 1);
+        const int32_t mn = sel(c, ta.minv[k0], ta.minv[k0 + 1]);
+        const uint32_t bs = uint32_t(sel(c, int32_t(ta.base[k0]), int32_t(ta.base[k0 + 1])));
+        bin = bs + uint32_t(fields[uint64_t(f) * stride + g] - mn);
+      }
+      const uint32_t rel = bin - lo;
+      if (rel < nb) {
+        if (lds) atomicAdd(&h[rel], 1u);
+        else atomicAdd(&counts[bin], 1u);
+      }
     }
   }
   if (lds) {
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < nbins; i += blockDim.x)
-      if (h[i]) atomicAdd(&counts[i], h[i]);
+    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x)
+      if (h[i]) atomicAdd(&counts[lo + i], h[i]);
   }
 }
 
-// Per-row sequential passes, one lane per row, rows staged through LDS in
-// chunks of 64 columns.  kRefit = false: sums[r] = sum of w^2 in column
-// order.  kRefit = true: least-squares row scale <W_r, sX_r> / <sX_r, sX_r>
-// with both sums in column order, X_r rebuilt from the fields.
+// Per-row sequential passes: lane l of wave 0 owns row r0 + l and adds in
+// column order; all four waves stage the next chunk of kRowChunk columns of
+// the block's 64 rows (and, for the refit, their fields) through registers
+// into the other half of a double buffer while wave 0 works on the current
+// one.  kRefit = false: sums[r] = sum of w^2.  kRefit = true: least-squares
+// row scale <W_r, sX_r> / <sX_r, sX_r>, X_r rebuilt from the fields.
 template <bool kRefit>
-__global__ __launch_bounds__(64) void row_pass_kernel(const float* __restrict__ Wq, int64_t rows, int64_t cols,
-                                                     const int32_t* __restrict__ fields, uint64_t stride,
-                                                     double s, double* __restrict__ sums,
-                                                     float* __restrict__ row_scales) {
-  __shared__ float wt[kRowBlock][kRowChunk + 1];
-  __shared__ int32_t ft[kRefit ? kFields : 1][kRowBlock][kRowChunk / 8 + 1];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__ Wq, int64_t rows, int64_t cols,
+                                                      const int32_t* __restrict__ fields, uint64_t stride,
+                                                      double s, double* __restrict__ sums,
+                                                      float* __restrict__ row_scales) {
+  constexpr int kVec = kRowChunk / 8;                       // vectors per row per chunk
+  constexpr int kW4 = kRowBlock * kRowChunk / 4 / 256;      // float4 loads per thread per chunk
+  constexpr int kF = kRefit ? kFields * kRowBlock * kVec / 256 : 1;   // field loads per thread
+  __shared__ float wt[2][kRowBlock][kRowChunk + 1];
+  __shared__ int32_t ft[2][kRefit ? kFields : 1][kRowBlock][kRefit ? kVec + 1 : 1];
+  const int tid = threadIdx.x;
   const int64_t r0 = int64_t(blockIdx.x) * kRowBlock;
-  const int64_t r = r0 + lane;
   const int nrow = int(std::min<int64_t>(kRowBlock, rows - r0));
   const uint64_t per_row = uint64_t(cols) / 8;
-  double acc = 0.0, num = 0.0, den = 0.0;
-  for (int64_t c0 = 0; c0 < cols; c0 += kRowChunk) {
+  const int nchunks = int((cols + kRowChunk - 1) / kRowChunk);
+  float4 wreg[kW4];
+  int32_t freg[kF];
+
+  auto gload = [&](int ch) {
+    const int64_t c0 = int64_t(ch) * kRowChunk;
     const int nc = int(std::min<int64_t>(kRowChunk, cols - c0));
-    __syncthreads();
-    for (int i = 0; i < nrow; ++i)
-      if (lane < nc) wt[i][lane] = Wq[(r0 + i) * cols + c0 + lane];
+#pragma unroll
+    for (int k = 0; k < kW4; ++k) {
+      const int row = (tid >> 5) + 8 * k, c4 = tid & 31;
+      if (row < nrow && 4 * c4 < nc)
+        wreg[k] = *reinterpret_cast<const float4*>(Wq + (r0 + row) * cols + c0 + 4 * c4);
+    }
     if (kRefit) {
       const int nv = nc / 8;
       const uint64_t j0 = uint64_t(c0) / 8;
-      for (int f = 0; f < kFields; ++f)
-        for (int i0 = 0; i0 < nrow; i0 += 8) {
-          const int i = i0 + (lane >> 3), v = lane & 7;
-          if (i < nrow && v < nv)
-            ft[f][i][v] = fields[uint64_t(f) * stride + uint64_t(r0 + i) * per_row + j0 + v];
-        }
+#pragma unroll
+      for (int k = 0; k < kF; ++k) {
+        const int f = k >> 2, rem = tid + 256 * (k & 3), row = rem >> 4, v = rem & 15;
+        if (row < nrow && v < nv) freg[k] = fields[uint64_t(f) * stride + uint64_t(r0 + row) * per_row + j0 + v];
+      }
     }
-    __syncthreads();
-    if (lane < nrow) {
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kW4; ++k) {
+      const int row = (tid >> 5) + 8 * k, c4 = tid & 31;
+      wt[buf][row][4 * c4 + 0] = wreg[k].x;
+      wt[buf][row][4 * c4 + 1] = wreg[k].y;
+      wt[buf][row][4 * c4 + 2] = wreg[k].z;
+      wt[buf][row][4 * c4 + 3] = wreg[k].w;
+    }
+    if (kRefit) {
+#pragma unroll
+      for (int k = 0; k < kF; ++k) {
+        const int f = k >> 2, rem = tid + 256 * (k & 3), row = rem >> 4, v = rem & 15;
+        ft[buf][f][row][v] = freg[k];
+      }
+    }
+  };
+
+  double acc = 0.0, num = 0.0, den = 0.0;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int buf = ch & 1;
+    const int nc = int(std::min<int64_t>(kRowChunk, cols - int64_t(ch) * kRowChunk));
+    if (ch + 1 < nchunks) gload(ch + 1);
+    if (tid < nrow) {
       if (!kRefit) {
         for (int q = 0; q < nc; ++q) {
-          const double w = double(wt[lane][q]);
+          const double w = double(wt[buf][tid][q]);
           acc += w * w;
         }
       } else {
         for (int v = 0; v < nc / 8; ++v) {
-          const int64_t c = ft[0][lane][v];
+          const int64_t c = ft[buf][0][tid][v];
           int64_t s7 = 0, x2[8];
 #pragma unroll
           for (int i = 1; i <= 7; ++i) {
-            const int64_t z = ft[i][lane][v];
+            const int64_t z = ft[buf][i][tid][v];
             s7 += z;
             x2[i - 1] = 2 * z + c;
           }
-          const int64_t z8 = 2 * int64_t(ft[8][lane][v]) + (s7 & 1);
+          const int64_t z8 = 2 * int64_t(ft[buf][8][tid][v]) + (s7 & 1);
           x2[7] = 2 * z8 + c;
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const double sx = s * (double(x2[q]) * 0.5);
-            num += double(wt[lane][8 * v + q]) * sx;
+            num += double(wt[buf][tid][8 * v + q]) * sx;
             den += sx * sx;
           }
         }
       }
     }
+    if (ch + 1 < nchunks) lstore(buf ^ 1);
+    __syncthreads();
   }
-  if (lane < nrow) {
-    if (!kRefit) sums[r] = acc;
-    else row_scales[r] = den > 0.0 ? float(num / den) : 0.0f;
+  if (tid < nrow) {
+    if (!kRefit) sums[r0 + tid] = acc;
+    else row_scales[r0 + tid] = den > 0.0 ? float(num / den) : 0.0f;
   }
 }
 
@@ -558,7 +603,7 @@ class DeviceEncoder {
     Wq_ = Wq;
     norms_.assign(size_t(std::max<int64_t>(S_.rows, 1)), 0.0);
     if (S_.rows > 0) {
-      row_pass_kernel<false><<<int((S_.rows + kRowBlock - 1) / kRowBlock), kRowBlock, 0, st_>>>(
+      row_pass_kernel<false><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
           Wq, S_.rows, S_.cols, nullptr, 0, 0.0, at<double>(L_.sums), nullptr);
       check(hipGetLastError(), "row_pass_kernel");
       check(hipMemcpyAsync(norms_.data(), at<double>(L_.sums), size_t(S_.rows) * 8, hipMemcpyDeviceToHost, st_),
@@ -621,8 +666,21 @@ class DeviceEncoder {
       ta.minv[k] = st.minv[k];
       ta.base[k] = st.base[k];
     }
-    histogram_kernel<<<grid_for(nq_, 256, 1024), 256, 0, st_>>>(at<int32_t>(L_.fields), fields_stride(), nq_, ta,
-                                                                st.sum, at<uint32_t>(L_.counts));
+    // tables are contiguous in bin space: group them so each pass fits in LDS
+    const int blocks = grid_for(nq_, 8192, 256);
+    for (int k0 = 0; k0 < kTables;) {
+      uint32_t lo = st.base[k0], hi = lo, fmask = 0;
+      int k1 = k0;
+      while (k1 < kTables && (k1 == k0 || hi + st.A[k1] - lo <= uint32_t(kHistBins))) {
+        hi += st.A[k1];
+        fmask |= 1u << (k1 == 0 ? 0 : 1 + (k1 - 1) / 2);
+        ++k1;
+      }
+      if (hi > lo)
+        histogram_kernel<<<blocks, 1024, 0, st_>>>(at<int32_t>(L_.fields), fields_stride(), nq_, ta, lo, hi, fmask,
+                                                   hi - lo <= uint32_t(kHistBins), at<uint32_t>(L_.counts));
+      k0 = k1;
+    }
     check(hipGetLastError(), "histogram_kernel");
     std::vector<uint32_t> c32(st.sum);
     check(hipMemcpyAsync(c32.data(), at<uint32_t>(L_.counts), size_t(st.sum) * 4, hipMemcpyDeviceToHost, st_),
@@ -657,7 +715,7 @@ class DeviceEncoder {
     I.vectors_per_tile = S_.V;
     I.num_tiles = uint32_t(S_.T);
     if (S_.rows > 0) {
-      row_pass_kernel<true><<<int((S_.rows + kRowBlock - 1) / kRowBlock), kRowBlock, 0, st_>>>(
+      row_pass_kernel<true><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
           Wq_, S_.rows, S_.cols, at<int32_t>(L_.fields), fields_stride(), double(s), nullptr, at<float>(L_.rscale));
       check(hipGetLastError(), "row_pass_kernel refit");
     }
