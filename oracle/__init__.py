@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(HERE, "libepo_oracle.so")
 SOURCES = ["epo_lattice.c", "epo_rans.c", "epo_codec.c", "epo_convert.c"]
 
 ROUTES = {"direct": 0, "fp8": 1, "int8": 2}
-OUT_KINDS = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "fp32": 101, "lattice2x": 100, "f32": 101,
+OUT_KINDS = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "uint8": 4, "fp32": 101, "lattice2x": 100, "f32": 101,
              "fields": 102}
-OUT_NUMPY = {"bf16": np.uint16, "fp8": np.uint8, "int8": np.int8, "fp16": np.uint16, "fp32": np.float32,
+OUT_NUMPY = {"bf16": np.uint16, "fp8": np.uint8, "int8": np.int8, "fp16": np.uint16, "uint8": np.uint8,
+             "fp32": np.float32,
              "lattice2x": np.int32, "f32": np.float32}
 TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1, 2, 3, 4
 NTABLES = 17
@@ -99,6 +100,7 @@ def _declare(L):
     L.epo_f32_to_f16_batch.argtypes = [vp, i64, vp]
     L.epo_f32_to_fp8e4m3_batch.argtypes = [vp, i64, vp]
     L.epo_f32_to_int8_batch.argtypes = [vp, i64, vp]
+    L.epo_f32_to_uint8_batch.argtypes = [vp, i64, vp]
     L.epo_fp8e4m3_value.argtypes = [C.c_uint8]
     L.epo_fp8e4m3_value.restype = f64
     L.epo_route_precast.argtypes = [vp, i64, i64, C.c_int, vp, vp]
@@ -381,6 +383,13 @@ def f32_to_fp8(y) -> np.ndarray:
     y = _c(y, np.float32)
     out = np.empty(y.shape, np.uint8)
     lib().epo_f32_to_fp8e4m3_batch(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def f32_to_uint8(y) -> np.ndarray:
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().epo_f32_to_uint8_batch(_ptr(y), y.size, _ptr(out))
     return out
 
 

@@ -41,6 +41,7 @@ enum { EPO_ROUTE_DIRECT = 0, EPO_ROUTE_FP8 = 1, EPO_ROUTE_INT8 = 2 };
 /* Decode output kinds. */
 enum {
   EPO_OUT_BF16 = 0, EPO_OUT_FP8 = 1, EPO_OUT_INT8 = 2, EPO_OUT_FP16 = 3,
+  EPO_OUT_UINT8 = 4,         /* unsigned 8-bit codes with offset 128 */
   EPO_OUT_LATTICE2X = 100,   /* int32, 2*x exactly */
   EPO_OUT_F32 = 101,         /* fp32 product x*g before container rounding */
   EPO_OUT_FIELDS = 102       /* int32 [nvec][9]: c, z1..z7, m */
@@ -107,6 +108,8 @@ int    epo_decode(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b
 uint16_t epo_f32_to_bf16(float y);
 uint8_t  epo_f32_to_fp8e4m3(float y);
 int8_t   epo_f32_to_int8(float y);
+uint8_t  epo_f32_to_uint8(float y);
+void     epo_f32_to_uint8_batch(const float* y, int64_t n, uint8_t* out);
 uint16_t epo_f32_to_f16(float y);
 void     epo_f32_to_f16_batch(const float* y, int64_t n, uint16_t* out);
 double   epo_fp8e4m3_value(uint8_t code);

@@ -548,6 +548,7 @@ int epo_decode(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b, f
           case EPO_OUT_BF16: ((uint16_t*)out)[o] = epo_f32_to_bf16(y); break;
           case EPO_OUT_FP8: ((uint8_t*)out)[o] = epo_f32_to_fp8e4m3(y); break;
           case EPO_OUT_INT8: ((int8_t*)out)[o] = epo_f32_to_int8(y); break;
+          case EPO_OUT_UINT8: ((uint8_t*)out)[o] = epo_f32_to_uint8(y); break;
           case EPO_OUT_FP16: ((uint16_t*)out)[o] = epo_f32_to_f16(y); break;
           default: ((float*)out)[o] = y; break;
         }

@@ -125,6 +125,20 @@ int8_t epo_f32_to_int8(float yf) {
   return (int8_t)r;
 }
 
+/* UINT8 container (paper, appendix A.6: unsigned integer dtypes carry an
+ * offset): the integer nearest y (ties to even) moved up by 128, then clamped
+ * to the unsigned byte range [0, 255]. */
+uint8_t epo_f32_to_uint8(float yf) {
+  double u = rint_even((double)yf) + 128.0;
+  if (u > 255.0) u = 255.0;
+  if (u < 0.0) u = 0.0;
+  return (uint8_t)u;
+}
+
+void epo_f32_to_uint8_batch(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = epo_f32_to_uint8(y[i]);
+}
+
 void epo_f32_to_bf16_batch(const float* y, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = epo_f32_to_bf16(y[i]);
 }

@@ -102,13 +102,14 @@ _DIT_BLOCK = (("qkv", 11520, 3840), ("out", 3840, 3840), ("up", 10240, 3840),
               ("gate", 10240, 3840), ("down", 3840, 10240))
 
 
-def _cfg3(blocks: int = 30) -> List[TensorSpec]:
+def _cfg3(blocks: int = 30, prob_bits: Optional[int] = None) -> List[TensorSpec]:
     # DiT linear set: blocks x {QKV 3840->11520, out, FFN up/gate 3840->10240, down}.
+    # prob_bits overrides the encoder's default precision (same weights).
     out = []
     i = 0
     for blk in range(blocks):
         for name, r, c in _DIT_BLOCK:
-            out.append(TensorSpec(f"b{blk}.{name}", r, c, 3000 + i, 4.0))
+            out.append(TensorSpec(f"b{blk}.{name}", r, c, 3000 + i, 4.0, prob_bits=prob_bits))
             i += 1
     return out
 
@@ -162,6 +163,7 @@ WORKLOADS = {
     "ref_layer_10240x3840_4bpp_bf16": lambda: _ref_layer(4),
     "ref_layer_10240x3840_8bpp_bf16": lambda: _ref_layer(8),
     "dit_linear_set_30x5_4bpp_bf16": lambda: _cfg3(30),
+    "dit_linear_set_30x5_4bpp_b9_bf16": lambda: _cfg3(30, 9),
     "llm_prefill_16x5_fp8route_5bpp": lambda: _cfg4(16),
     "mixed_300_int8route_2or8bpp": lambda: _cfg5(300),
 }

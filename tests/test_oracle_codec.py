@@ -110,6 +110,17 @@ def test_int8_rounding_matches_torch():
     assert np.array_equal(mine, ref)
 
 
+def test_uint8_rounding_matches_torch():
+    # unsigned container with offset 128 (appendix A.6): round half even, + 128, clamp to [0, 255]
+    y = np.concatenate([_f32_samples(), np.float32([-128.5, -129.0, 127.5, 128.0, -0.5, 0.5, 1e9, -1e9])])
+    mine = oracle.f32_to_uint8(y)
+    ref = (torch.clamp(torch.round(torch.from_numpy(y).double()) + 128, 0, 255)).to(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+    # the offset code of every in-range value is the INT8 code plus 128
+    inr = np.abs(y) < 127
+    assert np.array_equal(mine[inr].astype(np.int16), oracle.f32_to_int8(y[inr]).astype(np.int16) + 128)
+
+
 def _small(seed=0, rows=64, cols=256, outliers=0.0):
     return synthgen.student_t_weights(rows, cols, seed, outlier_frac=outliers).numpy()
 
