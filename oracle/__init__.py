@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libepo_oracle.so")
 SOURCES = ["epo_lattice.c", "epo_rans.c", "epo_codec.c", "epo_convert.c"]
 
 ROUTES = {"direct": 0, "fp8": 1, "int8": 2}
+# field codings: the method's, and the two ablations of the paper's Table 4
+CODINGS = {"standard": 0, "pooled": 1, "direct_z8": 2}
 OUT_KINDS = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "uint8": 4, "fp32": 101, "lattice2x": 100, "f32": 101,
              "fields": 102}
 OUT_NUMPY = {"bf16": np.uint16, "fp8": np.uint8, "int8": np.int8, "fp16": np.uint16, "uint8": np.uint8,
@@ -96,6 +98,15 @@ def _declare(L):
     L.epo_decode.argtypes = [i64, i64, u32, u32, u32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                              C.c_int, vp, vp, u32, u32]
     L.epo_decode.restype = C.c_int
+    L.epo_encode_coded.argtypes = [vp, i64, i64, f64, u32, u32, C.c_int, C.c_int, _p(vp)]
+    L.epo_encode_coded.restype = C.c_int
+    L.epo_tensor_coding.argtypes = [vp]
+    L.epo_tensor_coding.restype = C.c_int
+    L.epo_stored_bytes_coded.argtypes = [i64, u32, u64, vp, C.c_int, C.c_int]
+    L.epo_stored_bytes_coded.restype = u64
+    L.epo_decode_coded.argtypes = [i64, i64, u32, u32, u32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   C.c_int, C.c_int, vp, vp, u32, u32]
+    L.epo_decode_coded.restype = C.c_int
     L.epo_f32_to_bf16_batch.argtypes = [vp, i64, vp]
     L.epo_f32_to_f16_batch.argtypes = [vp, i64, vp]
     L.epo_f32_to_fp8e4m3_batch.argtypes = [vp, i64, vp]
@@ -219,9 +230,10 @@ def num_tiles(rows: int, cols: int, V: int) -> int:
     return int(lib().epo_num_tiles(rows, cols, V))
 
 
-def stored_bytes(rows: int, T: int, nwords: int, alphabet, route: str = "direct") -> int:
+def stored_bytes(rows: int, T: int, nwords: int, alphabet, route: str = "direct",
+                 coding: str = "standard") -> int:
     a = _c(alphabet, np.uint32)
-    return int(lib().epo_stored_bytes(rows, T, nwords, _ptr(a), ROUTES[route]))
+    return int(lib().epo_stored_bytes_coded(rows, T, nwords, _ptr(a), ROUTES[route], CODINGS[coding]))
 
 
 def sample_rows(rows: int, cols: int) -> np.ndarray:
@@ -260,6 +272,7 @@ class Container:
     alphabet: np.ndarray        # uint32 [17]
     minval: np.ndarray          # int32 [17]
     freq_base: np.ndarray       # uint32 [17]
+    coding: str = "standard"    # "pooled": coset slots share tables; "direct_z8": field 8 is z8
 
     @property
     def numel(self) -> int:
@@ -271,7 +284,7 @@ class Container:
 
     @property
     def stored_bytes(self) -> int:
-        return stored_bytes(self.rows, self.T, self.nwords, self.alphabet, self.route)
+        return stored_bytes(self.rows, self.T, self.nwords, self.alphabet, self.route, self.coding)
 
     @property
     def bpp(self) -> float:
@@ -303,17 +316,23 @@ def _from_handle(h) -> Container:
     fr = np.zeros(max(nf.value, 1), np.uint16)
     L.epo_tensor_copy(h, _ptr(rs), _ptr(qs), _ptr(st), _ptr(off), _ptr(pl), _ptr(fr))
     rname = {v: k for k, v in ROUTES.items()}[route.value]
+    cname = {v: k for k, v in CODINGS.items()}[L.epo_tensor_coding(h)]
     return Container(rows.value, cols.value, V.value, T.value, b.value, float(s.value), rname,
                      est.value, rs[: rows.value], None if qs is None else qs[: rows.value],
-                     st[: LANES * T.value], off, pl[: nw.value], fr[: nf.value], alpha, minv, fb)
+                     st[: LANES * T.value], off, pl[: nw.value], fr[: nf.value], alpha, minv, fb, cname)
 
 
-def encode(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct") -> Container:
-    """Compress a float32 [rows, cols] matrix at a target rate (scale search)."""
+def encode(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct",
+           coding: str = "standard") -> Container:
+    """Compress a float32 [rows, cols] matrix at a target rate (scale search).
+
+    coding selects the field coding (the method's, or a Table 4 ablation on the
+    same quantised points and row scales)."""
     W = _c(W, np.float32)
     R, Cc = W.shape
     h = C.c_void_p()
-    rc = lib().epo_encode(_ptr(W), R, Cc, float(target_bpp), V, b, ROUTES[route], C.byref(h))
+    rc = lib().epo_encode_coded(_ptr(W), R, Cc, float(target_bpp), V, b, ROUTES[route],
+                                CODINGS[coding], C.byref(h))
     if rc != 0:
         raise ValueError(f"oracle encode failed: {rc}")
     try:
@@ -353,12 +372,13 @@ def decode(ct: Container, kind: str = "bf16", tile_begin: int = 0, tile_end: Opt
     fr = ct.freqs if ct.freqs.size else np.zeros(1, np.uint16)
     rs = ct.row_scales if ct.row_scales.size else np.zeros(1, np.float32)
     st = ct.states if ct.states.size else np.zeros(1, np.uint32)
-    rc = lib().epo_decode(ct.rows, ct.cols, ct.V, ct.T, ct.b, ct.s, _ptr(_c(rs, np.float32)),
-                          _ptr(_c(st, np.uint32)), _ptr(_c(ct.offsets, np.uint32)),
-                          _ptr(_c(pl, np.uint16)), _ptr(_c(fr, np.uint16)),
-                          _ptr(_c(ct.freq_base, np.uint32)), _ptr(_c(ct.alphabet, np.uint32)),
-                          _ptr(_c(ct.minval, np.int32)), OUT_KINDS[kind], _ptr(out),
-                          _ptr(status), tile_begin, tile_end)
+    coding = CODINGS[getattr(ct, "coding", "standard")]
+    rc = lib().epo_decode_coded(ct.rows, ct.cols, ct.V, ct.T, ct.b, ct.s, _ptr(_c(rs, np.float32)),
+                                _ptr(_c(st, np.uint32)), _ptr(_c(ct.offsets, np.uint32)),
+                                _ptr(_c(pl, np.uint16)), _ptr(_c(fr, np.uint16)),
+                                _ptr(_c(ct.freq_base, np.uint32)), _ptr(_c(ct.alphabet, np.uint32)),
+                                _ptr(_c(ct.minval, np.int32)), coding, OUT_KINDS[kind], _ptr(out),
+                                _ptr(status), tile_begin, tile_end)
     if rc != 0:
         raise ValueError(f"oracle decode rejected its arguments: {rc}")
     return out, status[: ct.T]

@@ -38,6 +38,13 @@ static inline int epo_table_index(int f, int c) { return f == 0 ? 0 : 1 + 2 * (f
 /* Routes (paper, appendix B.1): direct, row-scaled FP8-e4m3, row-scaled INT8. */
 enum { EPO_ROUTE_DIRECT = 0, EPO_ROUTE_FP8 = 1, EPO_ROUTE_INT8 = 2 };
 
+/* Coding of the fields (paper, Table 4 and section "Parity reduction and coset
+ * conditioning"): the method's 17 coset-conditioned tables with m = floor(z8/2)
+ * as the eighth field, and the two ablations Table 4 measures on the same
+ * quantised points -- 9 tables pooled over the two cosets, and z8 coded
+ * directly instead of m. */
+enum { EPO_CODING_STANDARD = 0, EPO_CODING_POOLED = 1, EPO_CODING_DIRECT_Z8 = 2 };
+
 /* Decode output kinds. */
 enum {
   EPO_OUT_BF16 = 0, EPO_OUT_FP8 = 1, EPO_OUT_INT8 = 2, EPO_OUT_FP16 = 3,
@@ -89,6 +96,14 @@ int    epo_encode(const float* W, int64_t rows, int64_t cols, double target_bpp,
                   uint32_t V, uint32_t b0, int route, epo_tensor** out);
 int    epo_encode_fixed_scale(const float* W, int64_t rows, int64_t cols, float s,
                               uint32_t V, uint32_t b, int route, epo_tensor** out);
+/* epo_encode with a coding variant: the scale search, the points and the row
+ * scales are the standard coding's; only the tables and the payload differ. */
+int    epo_encode_coded(const float* W, int64_t rows, int64_t cols, double target_bpp,
+                        uint32_t V, uint32_t b0, int route, int coding, epo_tensor** out);
+int    epo_tensor_coding(const epo_tensor* t);
+/* Stored bytes of a coded container: pooled tables store 8 coordinate tables. */
+uint64_t epo_stored_bytes_coded(int64_t rows, uint32_t T, uint64_t nwords,
+                                const uint32_t alphabet[EPO_TABLES], int route, int coding);
 void   epo_tensor_free(epo_tensor* t);
 void   epo_tensor_info(const epo_tensor* t, int64_t* rows, int64_t* cols, uint32_t* V,
                        uint32_t* T, uint32_t* b, float* s, uint64_t* nwords,
@@ -103,6 +118,12 @@ int    epo_decode(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b
                   const uint16_t* payload, const uint16_t* freqs, const uint32_t* freq_base,
                   const uint32_t* alphabet, const int32_t* minval, int out_kind, void* out,
                   int32_t* tile_status, uint32_t tile_begin, uint32_t tile_end);
+/* epo_decode of a coded container (EPO_CODING_DIRECT_Z8: field 8 holds z8). */
+int    epo_decode_coded(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b, float s,
+                        const float* row_scales, const uint32_t* states, const uint32_t* offsets,
+                        const uint16_t* payload, const uint16_t* freqs, const uint32_t* freq_base,
+                        const uint32_t* alphabet, const int32_t* minval, int coding, int out_kind,
+                        void* out, int32_t* tile_status, uint32_t tile_begin, uint32_t tile_end);
 
 /* ---- dtype conversion (epo_convert.c) ---- */
 uint16_t epo_f32_to_bf16(float y);

@@ -65,6 +65,7 @@ struct epo_tensor {
   uint32_t freq_base[EPO_TABLES];
   uint16_t* freqs;
   uint32_t nfreqs;
+  int coding;
 };
 
 uint32_t epo_default_vectors_per_tile(double target_bpp) {
@@ -93,6 +94,14 @@ uint64_t epo_stored_bytes(int64_t rows, uint32_t T, uint64_t nwords,
   if (route != EPO_ROUTE_DIRECT) bytes += 4ull * (uint64_t)rows;  /* route scales */
   bytes += 132ull * T + 4;                   /* tile metadata (4J + 4 per tile) + final offset */
   bytes += 2ull * nwords;                    /* payload */
+  return bytes;
+}
+
+uint64_t epo_stored_bytes_coded(int64_t rows, uint32_t T, uint64_t nwords,
+                                const uint32_t alphabet[EPO_TABLES], int route, int coding) {
+  uint64_t bytes = epo_stored_bytes(rows, T, nwords, alphabet, route);
+  if (coding == EPO_CODING_POOLED)   /* the coset-1 copies of the 8 tables are not stored */
+    for (int f = 1; f < EPO_FIELDS; ++f) bytes -= 4 + 2 + 2ull * alphabet[epo_table_index(f, 1)];
   return bytes;
 }
 
@@ -268,7 +277,7 @@ static uint32_t max_coord_alphabet(const int32_t* fields, int64_t nvec) {
 /* Shared tail of the encoder: given the final fields at scale s and precision b,
  * fit row scales, build tables and encode tiles. */
 static int finish_encode(const float* Wq, int64_t rows, int64_t cols, float s, uint32_t b,
-                         uint32_t V, const int32_t* fields, epo_tensor* t) {
+                         uint32_t V, const int32_t* fields_in, int coding, epo_tensor* t) {
   int64_t per_row = cols / 8;
   int64_t nvec = rows * per_row;
   t->s = s;
@@ -282,7 +291,7 @@ static int finish_encode(const float* Wq, int64_t rows, int64_t cols, float s, u
   for (int64_t r = 0; r < rows; ++r) {
     double num = 0.0, den = 0.0;
     for (int64_t j = 0; j < per_row; ++j) {
-      epo_fields_to_point(fields + 9 * (r * per_row + j), x);
+      epo_fields_to_point(fields_in + 9 * (r * per_row + j), x);
       for (int q = 0; q < 8; ++q) {
         double sx = (double)s * x[q];
         num += (double)Wq[r * cols + 8 * j + q] * sx;
@@ -292,25 +301,70 @@ static int finish_encode(const float* Wq, int64_t rows, int64_t cols, float s, u
     t->row_scales[r] = den > 0.0 ? (float)(num / den) : 0.0f;
   }
 
+  /* the coded fields: direct z8 replaces m by z8 = 2m + parity(z1..z7) */
+  t->coding = coding;
+  const int32_t* fields = fields_in;
+  int32_t* zf = NULL;
+  if (coding == EPO_CODING_DIRECT_Z8) {
+    zf = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)(nvec ? nvec : 1));
+    memcpy(zf, fields_in, sizeof(int32_t) * 9 * (size_t)nvec);
+    for (int64_t g = 0; g < nvec; ++g) {
+      double x[8];
+      epo_fields_to_point(fields_in + 9 * g, x);
+      zf[9 * g + 8] = (int32_t)(x[7] - 0.5 * fields_in[9 * g]);
+    }
+    fields = zf;
+  }
+
   /* tables */
   int32_t maxv[EPO_TABLES];
   int has[EPO_TABLES];
   table_ranges(fields, nvec, t->minval, maxv, has);
+  if (coding == EPO_CODING_POOLED) {
+    /* one range per field over both cosets */
+    for (int f = 1; f < EPO_FIELDS; ++f) {
+      int k0 = epo_table_index(f, 0), k1 = epo_table_index(f, 1);
+      if (has[k0] && has[k1]) {
+        if (t->minval[k1] < t->minval[k0]) t->minval[k0] = t->minval[k1];
+        if (maxv[k1] > maxv[k0]) maxv[k0] = maxv[k1];
+      } else if (has[k1]) {
+        t->minval[k0] = t->minval[k1];
+        maxv[k0] = maxv[k1];
+        has[k0] = 1;
+      }
+      t->minval[k1] = t->minval[k0];
+      maxv[k1] = maxv[k0];
+      has[k1] = has[k0];
+    }
+  }
   alphabets_from_ranges(t->minval, maxv, has, t->alphabet);
   for (int k = 0; k < EPO_TABLES; ++k)
     if (!has[k]) t->minval[k] = 0;
   t->minval[0] = 0;
   uint64_t** counts = table_counts(fields, nvec, t->minval, t->alphabet);
+  if (coding == EPO_CODING_POOLED) {
+    /* pooled counts; the coset-1 slot shares the coset-0 table */
+    for (int f = 1; f < EPO_FIELDS; ++f) {
+      int k0 = epo_table_index(f, 0), k1 = epo_table_index(f, 1);
+      for (uint32_t i = 0; i < t->alphabet[k0]; ++i) counts[k0][i] += counts[k1][i];
+    }
+  }
   uint32_t nf = 0;
   for (int k = 0; k < EPO_TABLES; ++k) {
+    if (coding == EPO_CODING_POOLED && k > 0 && (k - 1) % 2 == 1) {
+      t->freq_base[k] = t->freq_base[k - 1];
+      continue;
+    }
     t->freq_base[k] = nf;
     nf += t->alphabet[k];
   }
   t->nfreqs = nf;
   t->freqs = (uint16_t*)calloc(nf ? nf : 1, sizeof(uint16_t));
   int rc = 0;
-  for (int k = 0; k < EPO_TABLES && rc == 0; ++k)
+  for (int k = 0; k < EPO_TABLES && rc == 0; ++k) {
+    if (coding == EPO_CODING_POOLED && k > 0 && (k - 1) % 2 == 1) continue;
     if (t->alphabet[k]) rc = epo_normalize_freqs(counts[k], t->alphabet[k], b, t->freqs + t->freq_base[k]);
+  }
   free_counts(counts);
   if (rc != 0) return -10;
 
@@ -345,6 +399,7 @@ static int finish_encode(const float* Wq, int64_t rows, int64_t cols, float s, u
   t->nwords = pos;
   epo__tables_free(tb);
   free(sym);
+  free(zf);
   return rc == 0 ? 0 : -11;
 }
 
@@ -371,6 +426,12 @@ static float* prepare_input(const float* W, int64_t rows, int64_t cols, int rout
 
 int epo_encode(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
                uint32_t b0, int route, epo_tensor** out) {
+  return epo_encode_coded(W, rows, cols, target_bpp, V, b0, route, EPO_CODING_STANDARD, out);
+}
+
+int epo_encode_coded(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
+                     uint32_t b0, int route, int coding, epo_tensor** out) {
+  if (coding < EPO_CODING_STANDARD || coding > EPO_CODING_DIRECT_Z8) return -1;
   if (rows < 0 || cols <= 0 || cols % 8 != 0) return -1;
   if (route < 0 || route > 2) return -1;
   if (V == 0) V = epo_default_vectors_per_tile(target_bpp);
@@ -409,7 +470,7 @@ int epo_encode(const float* W, int64_t rows, int64_t cols, double target_bpp, ui
     }
     break;
   }
-  int rc = finish_encode(Wq, rows, cols, s, b, V, fields, t);
+  int rc = finish_encode(Wq, rows, cols, s, b, V, fields, coding, t);
   free(fields);
   free(sample);
   free(norms);
@@ -437,7 +498,7 @@ int epo_encode_fixed_scale(const float* W, int64_t rows, int64_t cols, float s, 
   quantize_rows(Wq, cols, norms, NULL, rows, (double)s, fields);
   int rc = 0;
   if (max_coord_alphabet(fields, nvec) > (1u << b)) rc = -12;
-  if (rc == 0) rc = finish_encode(Wq, rows, cols, s, b, V, fields, t);
+  if (rc == 0) rc = finish_encode(Wq, rows, cols, s, b, V, fields, EPO_CODING_STANDARD, t);
   free(fields);
   free(norms);
   free(Wq);
@@ -476,6 +537,8 @@ void epo_tensor_info(const epo_tensor* t, int64_t* rows, int64_t* cols, uint32_t
   *est_bpp = t->est_bpp;
 }
 
+int epo_tensor_coding(const epo_tensor* t) { return t->coding; }
+
 void epo_tensor_tables(const epo_tensor* t, uint32_t* alphabet, int32_t* minval,
                        uint32_t* freq_base) {
   memcpy(alphabet, t->alphabet, sizeof(t->alphabet));
@@ -500,6 +563,17 @@ int epo_decode(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b, f
                const uint16_t* payload, const uint16_t* freqs, const uint32_t* freq_base,
                const uint32_t* alphabet, const int32_t* minval, int out_kind, void* out,
                int32_t* tile_status, uint32_t tile_begin, uint32_t tile_end) {
+  return epo_decode_coded(rows, cols, V, T, b, s, row_scales, states, offsets, payload, freqs,
+                          freq_base, alphabet, minval, EPO_CODING_STANDARD, out_kind, out,
+                          tile_status, tile_begin, tile_end);
+}
+
+int epo_decode_coded(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b, float s,
+                     const float* row_scales, const uint32_t* states, const uint32_t* offsets,
+                     const uint16_t* payload, const uint16_t* freqs, const uint32_t* freq_base,
+                     const uint32_t* alphabet, const int32_t* minval, int coding, int out_kind,
+                     void* out, int32_t* tile_status, uint32_t tile_begin, uint32_t tile_end) {
+  if (coding < EPO_CODING_STANDARD || coding > EPO_CODING_DIRECT_Z8) return -1;
   if (rows < 0 || cols <= 0 || cols % 8 != 0 || V < 32 || b < 9 || b > 15) return -1;
   if (T != epo_num_tiles(rows, cols, V)) return -1;
   if (tile_begin > tile_end || tile_end > T) return -1;
@@ -534,7 +608,12 @@ int epo_decode(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_t b, f
         continue;
       }
       double x[8];
-      epo_fields_to_point(fl, x);
+      if (coding == EPO_CODING_DIRECT_Z8) {
+        /* the eighth field is z8 itself: x = z + c/2 for all eight coordinates */
+        for (int i = 0; i < 8; ++i) x[i] = (double)fl[1 + i] + 0.5 * c;
+      } else {
+        epo_fields_to_point(fl, x);
+      }
       uint64_t r = g / (uint64_t)per_row;
       float gs = s * row_scales[r];              /* fp32(s * r_row) */
       for (int q = 0; q < 8; ++q) {
