@@ -424,6 +424,55 @@ def encode_timing(threads: int, reps: int):
     print(json.dumps({"encode": out}), flush=True)
 
 
+def coding_ablations(reps: int):
+    """The paper's Table 4 on the reference layer shape: stored rate of the three codings.
+
+    Each target is compressed by the device compressor in the standard coding
+    and in the two ablations (9 pooled tables; z8 coded directly), which keep
+    the same quantised points and row scales.  Reported per coding: stored bpp
+    and its difference to the standard coding, and the decode-kernel time of the
+    container to BF16.  Every variant's decoded lattice must equal the standard
+    coding's.
+    """
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+
+    spec = synthgen.workload("ref_layer_10240x3840_4bpp_bf16")[0]
+    W = spec.weights(device="cuda:0")
+    need = max(ep.encode_device_workspace_size(spec.rows, spec.cols, t) for t in (2.0, 4.0, 8.0))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    sp = ep.C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows = []
+    for target in (2.0, 4.0, 8.0):
+        base_lat, base_bpp = None, None
+        for coding in ("standard", "pooled", "direct_z8"):
+            d = ep.encode_device(W, target, workspace=ws, coding=coding)
+            p = d.packed
+            lat, st = ep.decode_tensor(p, "lattice2x", with_status=True)
+            torch.cuda.synchronize()
+            ok = bool((st[: p.T] == 0).all())
+            if base_lat is None:
+                base_lat = lat
+            same = bool(torch.equal(lat, base_lat))
+            del lat
+            o = torch.empty((p.rows, p.cols), dtype=torch.bfloat16, device="cuda:0")
+            wsd = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda:0")
+            batch = ep.BatchArgs([p], ["bf16"], [o], None, wsd)
+            plan = batch.prepare(sp)
+            t_launch = _time_ms(lambda: batch.launch(plan, sp), reps)
+            bpp = 8.0 * p.stored_bytes / p.numel
+            if base_bpp is None:
+                base_bpp = bpp
+            rows.append({"target_bpp": target, "coding": coding, "b": p.b, "stored_bpp": bpp,
+                         "delta_bpp": bpp - base_bpp, "decode_launch_ms": t_launch,
+                         "same_points": same, "tiles_ok": ok})
+            log(json.dumps(rows[-1]))
+            del o, wsd, batch, d, p
+    print(json.dumps({"coding_ablations": {"layer": [spec.rows, spec.cols], "points": rows}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,7 +495,13 @@ def main():
                     help="only sweep the tile size S (coordinates), e.g. 4096,8192,16384,32768")
     ap.add_argument("--encode", action="store_true",
                     help="only time the device compressor per layer beside the host compressor")
+    ap.add_argument("--ablations", action="store_true",
+                    help="only measure the Table 4 coding ablations on the reference layer shape")
     args = ap.parse_args()
+
+    if args.ablations:
+        coding_ablations(max(args.steps, 1))
+        return
 
     if args.encode:
         encode_timing(args.threads, max(args.steps, 1))
@@ -487,7 +542,7 @@ def main():
     packed, hosts = build_inputs(specs, args.threads, device, args.cache, args.host_encoder)
     numel = sum(p.numel for p in packed)
     stored = sum(p.stored_bytes for p in packed)
-    out_bytes = sum(p.numel * {"bf16": 2, "fp8": 1, "int8": 1}[d] for p, d in zip(packed, dtypes))
+    out_bytes = sum(p.numel * {"bf16": 2, "fp16": 2, "fp32": 4, "fp8": 1, "int8": 1, "uint8": 1}[d] for p, d in zip(packed, dtypes))
     outs = ep.alloc_outputs(packed, dtypes, device)
     ws = torch.empty(ep.workspace_size(packed), dtype=torch.uint8, device=device)
     batch = ep.BatchArgs(packed, dtypes, outs, None, ws)

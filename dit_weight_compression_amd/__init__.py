@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libentropack_mi355x.so")
 NTABLES = 17
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE, EP_ERR_HIP = 0, -1, -2, -3, -4
-DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "fp32": 4, "lattice2x": 100}
+DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "fp16": 3, "fp32": 4, "uint8": 5, "lattice2x": 100}
 TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1, 2, 3, 4
 
 # every symbol include/entropack.h declares
@@ -29,6 +29,7 @@ EXPORTS = ["ep_status_string", "ep_last_error", "ep_abi_version", "ep_workspace_
 DEVICE_ENCODE_EXPORTS = ["ep_encode_device_workspace_size", "ep_encode_device",
                          "ep_encode_device_emit"]
 ROUTES = {"direct": 0, "fp8": 1, "int8": 2}
+CODINGS = {"standard": 0, "pooled": 1, "direct_z8": 2}   # ep_coding
 
 
 class EpError(RuntimeError):
@@ -54,6 +55,7 @@ class EpTensorDesc(C.Structure):
         ("freq_base", C.c_uint32 * NTABLES),
         ("alphabet", C.c_uint32 * NTABLES),
         ("min_offset", C.c_int32 * NTABLES),
+        ("field8", C.c_uint32),
     ]
 
 
@@ -92,7 +94,7 @@ def lib():
                                                       C.c_int, C.POINTER(C.c_size_t)]
         L.ep_encode_device_workspace_size.restype = C.c_int
         L.ep_encode_device.argtypes = [vp, C.c_int64, C.c_int64, C.c_double, C.c_uint32, C.c_uint32,
-                                       C.c_int, vp, C.c_size_t, vp, vp]
+                                       C.c_int, C.c_int, vp, C.c_size_t, vp, vp]
         L.ep_encode_device.restype = C.c_int
         L.ep_encode_device_emit.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_encode_device_emit.restype = C.c_int
@@ -135,6 +137,7 @@ class PackedTensor:
         return self.rows * self.cols
 
     nwords: int = 0         # payload words (the device buffer is padded to a multiple of 8)
+    field8: int = 0         # 1: field 8 holds z8 (the direct-z8 coding), 0: m
 
     @classmethod
     def from_arrays(cls, ct, device="cuda", stored_bytes: int = 0) -> "PackedTensor":
@@ -158,7 +161,7 @@ class PackedTensor:
                    np.asarray(ct.freq_base, np.uint32).copy(),
                    up(ct.row_scales, np.float32, np.float32), up(ct.states, np.uint32, np.int32),
                    up(ct.offsets, np.uint32, np.int32), payload, up(ct.freqs, np.uint16, np.int16),
-                   stored_bytes, nw)
+                   stored_bytes, nw, 1 if getattr(ct, "coding", "standard") == "direct_z8" else 0)
 
     def desc(self) -> EpTensorDesc:
         d = EpTensorDesc()
@@ -175,13 +178,15 @@ class PackedTensor:
             d.freq_base[k] = int(self.freq_base[k])
             d.alphabet[k] = int(self.alphabet[k])
             d.min_offset[k] = int(self.minval[k])
+        d.field8 = int(self.field8)
         return d
 
 
 def torch_dtype(name: str):
     torch = _torch()
     return {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8,
-            "fp16": torch.float16, "fp32": torch.float32, "lattice2x": torch.int32}[name]
+            "fp16": torch.float16, "fp32": torch.float32, "uint8": torch.uint8,
+            "lattice2x": torch.int32}[name]
 
 
 def workspace_size(packed: Sequence[PackedTensor]) -> int:
@@ -298,14 +303,16 @@ class DeviceEncoded:
     route_scales: "object"   # torch float32 [rows] (FP8 / INT8 routes), else None
     est_bpp: float
     num_freqs: int
+    coding: str = "standard"
 
 
 def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct",
-                  workspace=None, stream=None) -> DeviceEncoded:
+                  workspace=None, stream=None, coding: str = "standard") -> DeviceEncoded:
     """Compress a float32 device tensor [rows, cols] with ep_encode_device.
 
     The container matches the host compressor's byte for byte; its arrays are
-    left on W's device, ready for decode_tensor / decode_batch.
+    left on W's device, ready for decode_tensor / decode_batch.  coding selects
+    a Table 4 ablation ("pooled", "direct_z8") on the same points and scales.
     """
     from .encoder import EncodedInfo
     torch = _torch()
@@ -322,8 +329,8 @@ def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "di
     sp = C.c_void_p(stream.cuda_stream)
     info = EncodedInfo()
     _check(lib().ep_encode_device(W.data_ptr() if W.numel() else None, R, Cc, float(target_bpp), V, b,
-                                  ROUTES[route], workspace.data_ptr(), workspace.numel(), sp,
-                                  C.byref(info)))
+                                  ROUTES[route], CODINGS[coding], workspace.data_ptr(), workspace.numel(),
+                                  sp, C.byref(info)))
     T, nw, nf = info.num_tiles, int(info.payload_words), info.num_freqs
     rs = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
     qs = torch.empty(max(R, 1), dtype=torch.float32, device=dev) if route != "direct" else None
@@ -338,8 +345,8 @@ def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "di
     p = PackedTensor(R, Cc, info.vectors_per_tile, T, info.prob_bits, float(info.scale),
                      np.array(info.alphabet, np.uint32), np.array(info.min_offset, np.int32),
                      np.array(info.freq_base, np.uint32), rs, st, off, pl, fr,
-                     int(info.stored_bytes), nw)
-    return DeviceEncoded(p, route, qs, float(info.estimated_bpp), nf)
+                     int(info.stored_bytes), nw, 1 if coding == "direct_z8" else 0)
+    return DeviceEncoded(p, route, qs, float(info.estimated_bpp), nf, coding)
 
 
 ep_encode_device = encode_device

@@ -88,7 +88,7 @@ struct alignas(16) DevTensor {
   uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
   uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
   uint32_t slow_rows;        // set by the table build: rowv holds g, not g/2
-  uint32_t pad0;
+  uint32_t f8z8;             // 1: field 8 holds z8 (no parity reduction), 0: it holds m
   uint64_t payload_words;
   const float* row_scales;
   float* rowv;               // workspace: per-row multiplier g/2 (or g), g = fp32(scale * row scale)
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         const uint32_t zpar = (tl == kTabNarrow && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
         sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
         const int32_t z = int32_t(i) + mn;
-        val[i] = float(field < 8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
+        val[i] = float(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
       }
     }
     __syncthreads();
@@ -283,7 +283,8 @@ constexpr uint32_t kRingSlack = kRingWords - kChunkWords; // a chunk fits while 
 constexpr size_t kRingBytes = size_t(kTilesPerChunk) * kRingWords * sizeof(uint16_t);
 
 enum OutKind : int {
-  kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kOutFP16 = 4, kOutFP32 = 5, kNumOutKinds = 6
+  kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kOutFP16 = 4, kOutFP32 = 5, kOutUINT8 = 6,
+  kNumOutKinds = 7
 };
 
 __host__ __device__ constexpr uint32_t out_vec_bytes(int ok) {
@@ -360,6 +361,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   uint32_t f0v = f0, f1v = M - f0;                          // per-lane copies for the selects
   asm volatile("" : "+v"(f0v), "+v"(f1v));
   const uint32_t kpar = T.kpar;
+  // field 8: m (value 4 s + 2 parity + const) or z8 itself (2 s + const, no parity)
+  const uint32_t pw = T.f8z8 ? 0u : 1u;                     // width of the parity bit field
+  const uint32_t sh8 = T.f8z8 ? 1u : 2u;
   const uint32_t empty = T.empty_mask;
   const bool slow_rows = T.slow_rows != 0;
   const unsigned char* tbase = kWs ? T.tab : lds;
@@ -495,10 +499,11 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
           __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
           __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
           ev[7] ^ kp, 0x96);
-      par = __builtin_amdgcn_ubfe(x3, kSymShift, 1);
+      par = __builtin_amdgcn_ubfe(x3, kSymShift, pw);
       // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + (c + 4 min), the
-      // parenthesis being part of the per-table constant
-      const uint32_t u8 = ((ev[8] >> kSymShift) << 2) + ((par << 1) | 0x4B400000u);
+      // parenthesis being part of the per-table constant (a directly coded
+      // z8: 2 s8 + (c + 2 min), with the parity field of width 0)
+      const uint32_t u8 = ((ev[8] >> kSymShift) << sh8) + ((par << 1) | 0x4B400000u);
       const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
       vv[8] = __builtin_bit_cast(float, u8) - k8;
     } else {
@@ -527,8 +532,8 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
                                                       sv[7], 0x96);
       // narrow: bit 15 of the symbol entries is the parity of z; workspace:
       // parity of the symbol indices, corrected by the parity of the minima
-      par = TL == kTabNarrow ? __builtin_amdgcn_ubfe(x3, 15, 1) : (x3 ^ (kpar >> (c ? 1 : 0))) & 1u;
-      vv[8] = vv[8] + float(par << 1);                   // the m table holds 4 m + c
+      par = TL == kTabNarrow ? __builtin_amdgcn_ubfe(x3, 15, pw) : (x3 ^ (kpar >> (c ? 1 : 0))) & pw;
+      vv[8] = vv[8] + float(par << 1);                   // the m table holds 4 m + c (z8: 2 z8 + c)
     }
 #undef EP_RENORM
     x = active ? x : x_saved;
@@ -570,8 +575,10 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
                              (fp8_e4m3_rne(y[7]) << 24)};
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       } else {
-        const u32x2 w = {int8_rne(y[0]) | (int8_rne(y[1]) << 8) | (int8_rne(y[2]) << 16) | (int8_rne(y[3]) << 24),
-                         int8_rne(y[4]) | (int8_rne(y[5]) << 8) | (int8_rne(y[6]) << 16) | (int8_rne(y[7]) << 24)};
+        // INT8 codes; UINT8 adds the offset 128, i.e. flips each byte's top bit
+        const uint32_t off = OK == kOutUINT8 ? 0x80808080u : 0u;
+        const u32x2 w = {(int8_rne(y[0]) | (int8_rne(y[1]) << 8) | (int8_rne(y[2]) << 16) | (int8_rne(y[3]) << 24)) ^ off,
+                         (int8_rne(y[4]) | (int8_rne(y[5]) << 8) | (int8_rne(y[6]) << 16) | (int8_rne(y[7]) << 24)) ^ off};
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       }
     }
@@ -664,6 +671,7 @@ int out_kind_of(int dtype) {
     case EP_OUT_LATTICE2X_I32: return kOutLattice;
     case EP_OUT_FP16: return kOutFP16;
     case EP_OUT_FP32: return kOutFP32;
+    case EP_OUT_UINT8: return kOutUINT8;
     default: return -1;
   }
 }
@@ -692,6 +700,7 @@ int validate(const ep_tensor_desc& d, int i) {
   const uint64_t T = (nv + d.vectors_per_tile - 1) / d.vectors_per_tile;
   if (T != d.num_tiles) return bad("num_tiles != ceil(rows*cols/8 / vectors_per_tile)");
   if (d.alphabet[0] != 2 || d.min_offset[0] != 0) return bad("table 0 must be the coset bit (alphabet 2, min 0)");
+  if (d.field8 != EP_FIELD8_M && d.field8 != EP_FIELD8_Z8) return bad("field8 must be EP_FIELD8_M or EP_FIELD8_Z8");
   for (int k = 1; k < kTables; ++k) {
     if (d.alphabet[k] > (1u << d.prob_bits)) return bad("alphabet exceeds 2^prob_bits");
     // |4 z + c| < 2^22 keeps every reconstructed value exact in fp32
@@ -770,6 +779,7 @@ KernelFn kernel_for_kind(int ok) {
     case kOutINT8: return decode_kernel<BT, TL, kOutINT8>;
     case kOutFP16: return decode_kernel<BT, TL, kOutFP16>;
     case kOutFP32: return decode_kernel<BT, TL, kOutFP32>;
+    case kOutUINT8: return decode_kernel<BT, TL, kOutUINT8>;
     default: return decode_kernel<BT, TL, kOutLattice>;
   }
 }
@@ -919,6 +929,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.tab = reinterpret_cast<unsigned char*>(wsb + L.tab_off[i]);
     D.rowv = reinterpret_cast<float*>(wsb + L.row_off[i]);
     D.slow_rows = 0;
+    D.f8z8 = d.field8 == EP_FIELD8_Z8 ? 1u : 0u;
     D.out = outs[i];
     D.status = tile_status ? tile_status[i] : nullptr;
     uint32_t em = 0, kpar = 0;
@@ -939,7 +950,9 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       const int64_t mn = d.min_offset[1 + t], c = t & 1;
       // f = 2^11 (a one-symbol table at b = 11) sets bit 22 of the packed entry
       const int64_t fb = (d.prob_bits == 11 && d.alphabet[1 + t] == 1) ? 1 : 0;
-      const int64_t kv = t >= 14 ? 12582912 - (4 * mn + c) : wide ? 12582912 - mn : 12582912 + fb - (2 * mn + c);
+      // field 8: 4 m + c (2 z8 + c when z8 is coded directly)
+      const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
+      const int64_t kv = t >= 14 ? 12582912 - (k8 * mn + c) : wide ? 12582912 - mn : 12582912 + fb - (2 * mn + c);
       const float kf = float(kv);                   // exact: kv lies in [2^23, 2^24)
       std::memcpy(&D.kvals[t], &kf, 4);
     }

@@ -92,9 +92,13 @@ inline int normalize_table(const uint64_t* counts, uint32_t A, uint32_t b, uint1
 // table a 4-byte minimum, a 2-byte alphabet size and 2 bytes per symbol, 4
 // bytes per row scale (twice with a route pre-cast), 132 bytes per tile
 // (32 states and one offset), the closing offset and the payload words.
-inline uint64_t stored_bytes(int64_t rows, uint64_t T, uint64_t words, const uint32_t* A, bool route) {
+// With pooled tables (the Table 4 ablation) only the coset-0 copy of each
+// coordinate table is stored.
+inline uint64_t stored_bytes(int64_t rows, uint64_t T, uint64_t words, const uint32_t* A, bool route,
+                             bool pooled = false) {
   uint64_t bytes = 32 + 4;
-  for (int k = 1; k < kTables; ++k) bytes += 6 + 2ull * A[k];
+  for (int k = 1; k < kTables; ++k)
+    if (!(pooled && (k - 1) % 2 == 1)) bytes += 6 + 2ull * A[k];
   bytes += 4ull * uint64_t(rows);
   if (route) bytes += 4ull * uint64_t(rows);
   bytes += 132ull * T + 4 + 2ull * words;

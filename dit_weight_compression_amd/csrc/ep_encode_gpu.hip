@@ -280,6 +280,45 @@ __global__ __launch_bounds__(1024) void histogram_kernel(const int32_t* __restri
   }
 }
 
+// Direct-z8 coding (the Table 4 ablation): field 8 becomes z8 = 2 m +
+// parity(z1..z7) in place, with its per-coset range: ranges[15 + c] = min,
+// ranges[17 + 15 + c] = -max (atomicMin).
+__global__ __launch_bounds__(256) void z8_kernel(int32_t* __restrict__ fields, uint64_t stride, uint64_t nq,
+                                                int32_t* __restrict__ ranges) {
+  int32_t lo[2] = {INT32_MAX, INT32_MAX}, nhi[2] = {INT32_MAX, INT32_MAX};
+  for (uint64_t g = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; g < nq;
+       g += uint64_t(gridDim.x) * blockDim.x) {
+    const int c = fields[g];
+    int32_t par = 0;
+#pragma unroll
+    for (int f = 1; f <= 7; ++f) par ^= fields[uint64_t(f) * stride + g];
+    const int32_t z8 = 2 * fields[8 * stride + g] + (par & 1);
+    fields[8 * stride + g] = z8;
+    if (c) {
+      lo[1] = min(lo[1], z8);
+      nhi[1] = min(nhi[1], -z8);
+    } else {
+      lo[0] = min(lo[0], z8);
+      nhi[0] = min(nhi[0], -z8);
+    }
+  }
+  __shared__ int32_t red[4][4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int32_t v[4] = {lo[0], lo[1], nhi[0], nhi[1]};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    for (int o = 32; o > 0; o >>= 1) v[i] = min(v[i], __shfl_xor(v[i], o));
+    if (lane == 0) red[wv][i] = v[i];
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    int32_t m = red[0][threadIdx.x];
+    for (int w = 1; w < 4; ++w) m = min(m, red[w][threadIdx.x]);
+    const int k = 15 + (threadIdx.x & 1);
+    if (m != INT32_MAX) atomicMin(&ranges[threadIdx.x < 2 ? k : kTables + k], m);
+  }
+}
+
 // Per-row sequential passes: lane l of wave 0 owns row r0 + l and adds in
 // column order; all four waves stage the next chunk of kRowChunk columns of
 // the block's 64 rows (and, for the refit, their fields) through registers
@@ -708,9 +747,10 @@ class DeviceEncoder {
     return amax;
   }
 
-  // Row refit, final tables, tile encode and offsets.
-  int finish(float s, uint32_t b, const Stats& st, ep_encoded_info& I) {
+  // Row refit, final tables (in the requested coding), tile encode and offsets.
+  int finish(float s, uint32_t b, Stats st, int coding, ep_encoded_info& I) {
     I.scale = s;
+    I.coding = coding;
     I.prob_bits = b;
     I.vectors_per_tile = S_.V;
     I.num_tiles = uint32_t(S_.T);
@@ -719,23 +759,71 @@ class DeviceEncoder {
           Wq_, S_.rows, S_.cols, at<int32_t>(L_.fields), fields_stride(), double(s), nullptr, at<float>(L_.rscale));
       check(hipGetLastError(), "row_pass_kernel refit");
     }
-    const std::vector<uint64_t> cnt = counts(st);
+    const bool pooled = coding == EP_CODING_POOLED;
+    if (coding == EP_CODING_DIRECT_Z8 && S_.nvec > 0) {
+      // field 8 becomes z8 (after the refit, which uses m); new ranges for tables 15, 16
+      check(hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(at<int32_t>(L_.ranges)), INT32_MAX, 2 * kTables,
+                              st_),
+            "clear ranges");
+      z8_kernel<<<grid_for(S_.nvec, 256, 2048), 256, 0, st_>>>(at<int32_t>(L_.fields), fields_stride(), S_.nvec,
+                                                                at<int32_t>(L_.ranges));
+      check(hipGetLastError(), "z8_kernel");
+      int32_t rg[2 * kTables];
+      check(hipMemcpyAsync(rg, at<int32_t>(L_.ranges), sizeof(rg), hipMemcpyDeviceToHost, st_), "copy ranges");
+      check(hipStreamSynchronize(st_), "z8");
+      for (int k = 15; k < kTables; ++k) {
+        const int32_t mn = rg[k], mx = rg[kTables + k] == INT32_MAX ? INT32_MIN : -rg[kTables + k];
+        const bool has = mn <= mx;
+        st.minv[k] = has ? mn : 0;
+        st.A[k] = has ? uint32_t(int64_t(mx) - int64_t(mn) + 1) : 0u;
+      }
+      bases(st);
+    }
+    if (pooled) {
+      // one range per field over both cosets; the two slots keep separate count regions
+      for (int f = 1; f < kFields; ++f) {
+        const int k0 = 1 + 2 * (f - 1), k1 = k0 + 1;
+        if (st.A[k0] && st.A[k1]) {
+          const int64_t mn = std::min(st.minv[k0], st.minv[k1]);
+          const int64_t mx = std::max(int64_t(st.minv[k0]) + st.A[k0], int64_t(st.minv[k1]) + st.A[k1]) - 1;
+          st.minv[k0] = int32_t(mn);
+          st.A[k0] = uint32_t(mx - mn + 1);
+        } else if (st.A[k1]) {
+          st.minv[k0] = st.minv[k1];
+          st.A[k0] = st.A[k1];
+        }
+        st.minv[k1] = st.minv[k0];
+        st.A[k1] = st.A[k0];
+      }
+      bases(st);
+    }
+    for (int k = 1; k < kTables; ++k)
+      if (st.A[k] > (1u << b)) return EP_ERR_UNSUPPORTED;   // an ablation's alphabet outgrew 2^b
+    std::vector<uint64_t> cnt = counts(st);
     uint32_t nf = 0;
     for (int k = 0; k < kTables; ++k) {
       I.alphabet[k] = st.A[k];
       I.min_offset[k] = st.minv[k];
+      if (pooled && k > 0 && (k - 1) % 2 == 1) {   // the coset-1 slot shares the coset-0 table
+        I.freq_base[k] = I.freq_base[k - 1];
+        for (uint32_t i = 0; i < st.A[k]; ++i) cnt[st.base[k - 1] + i] += cnt[st.base[k] + i];
+        continue;
+      }
       I.freq_base[k] = nf;
       nf += st.A[k];
     }
     I.num_freqs = nf;
     if (nf > S_.ntab) return EP_ERR_UNSUPPORTED;
     freqs_.assign(std::max<uint32_t>(nf, 1u), 0);
-    for (int k = 0; k < kTables; ++k)
+    for (int k = 0; k < kTables; ++k) {
+      if (pooled && k > 0 && (k - 1) % 2 == 1) continue;
       if (st.A[k] &&
           ep_common::normalize_table(cnt.data() + st.base[k], st.A[k], b, &freqs_[I.freq_base[k]]) != 0)
         return EP_ERR_UNSUPPORTED;
+    }
     tab_.assign(std::max<uint32_t>(nf, 1u), 0);
     for (int k = 0; k < kTables; ++k) {
+      if (pooled && k > 0 && (k - 1) % 2 == 1) continue;
       uint32_t cum = 0;
       for (uint32_t i = 0; i < st.A[k]; ++i) {
         const uint32_t f = freqs_[I.freq_base[k] + i];
@@ -771,7 +859,7 @@ class DeviceEncoder {
     const uint64_t words = uint64_t(flags[0]) | (uint64_t(flags[1]) << 32);
     if (words > 0xFFFFFFFFull) return EP_ERR_UNSUPPORTED;
     I.payload_words = words;
-    I.stored_bytes = ep_common::stored_bytes(S_.rows, S_.T, words, I.alphabet, S_.route != EP_ROUTE_DIRECT);
+    I.stored_bytes = ep_common::stored_bytes(S_.rows, S_.T, words, I.alphabet, S_.route != EP_ROUTE_DIRECT, pooled);
     return EP_OK;
   }
 
@@ -814,9 +902,11 @@ int ep_encode_device_workspace_size(int64_t rows, int64_t cols, double target_bp
 }
 
 int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
-                     uint32_t prob_bits, int route, void* workspace, size_t ws_bytes, void* stream,
+                     uint32_t prob_bits, int route, int coding, void* workspace, size_t ws_bytes, void* stream,
                      ep_encoded_info* info) {
   if (!info) return ep_record_error(EP_ERR_INVALID_ARG, "info is NULL");
+  if (coding < EP_CODING_STANDARD || coding > EP_CODING_DIRECT_Z8)
+    return ep_record_error(EP_ERR_INVALID_ARG, "coding must be an ep_coding");
   if (!W && rows > 0) return ep_record_error(EP_ERR_INVALID_ARG, "W is NULL");
   if (W && (reinterpret_cast<uintptr_t>(W) & 15))
     return ep_record_error(EP_ERR_INVALID_ARG, "W must be 16-byte aligned");
@@ -858,7 +948,7 @@ int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_b
       }
       break;
     }
-    rc = E.finish(s, b, st, I);
+    rc = E.finish(s, b, st, coding, I);
     if (rc != EP_OK) return ep_record_error(rc, "a table could not be normalised or the payload is too long");
   } catch (const HipFailure& f) {
     return ep_record_error(f.code, f.msg);

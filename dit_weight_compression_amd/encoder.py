@@ -24,6 +24,7 @@ class EncodedInfo(C.Structure):
         ("scale", C.c_float), ("route", C.c_int32), ("estimated_bpp", C.c_double),
         ("payload_words", C.c_uint64), ("num_freqs", C.c_uint32), ("stored_bytes", C.c_uint64),
         ("alphabet", C.c_uint32 * 17), ("min_offset", C.c_int32 * 17), ("freq_base", C.c_uint32 * 17),
+        ("coding", C.c_int32),
     ]
 
 

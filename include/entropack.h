@@ -26,11 +26,13 @@
  *     codes the coset bit c (alphabet 2), table 1 + 2*(f-1) + c codes field f
  *     (1..7 = z1..z7, 8 = m) of vectors in coset c; symbol i of table k stands
  *     for the value i + min_offset[k]; alphabet[k] = 0 marks an empty table;
- *   - reconstruction: z8 = 2m + ((z1 + ... + z7) & 1), x_i = z_i + c/2,
+ *   - reconstruction: z8 = 2m + ((z1 + ... + z7) & 1) (or z8 as stored, see
+ *     ep_tensor_desc.field8), x_i = z_i + c/2,
  *     y = fp32(x_i * fp32(scale * row_scales[row])), then the container
  *     rounding (BF16 round-to-nearest-even; FP8 OCP e4m3fn clamped to +-448
  *     then round-to-nearest-even; INT8 round-half-even then clamp to
- *     [-128, 127]).
+ *     [-128, 127]; UINT8 the same integer plus the offset 128, clamped to
+ *     [0, 255], the unsigned container of appendix A.6).
  *
  * Ownership: the caller owns every buffer.  Device pointers must stay valid
  * until the work enqueued on `stream` has finished.  The library never
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 #define EP_NUM_TABLES 17
 #define EP_LANES 32
 
@@ -72,6 +74,7 @@ typedef enum {
   EP_OUT_INT8 = 2,           /* int8 codes, [rows, cols] */
   EP_OUT_FP16 = 3,           /* uint16 IEEE binary16 bit patterns (RNE, overflow to inf), [rows, cols] */
   EP_OUT_FP32 = 4,           /* float32 products y = fp32(x * fp32(s * r_row)), [rows, cols] */
+  EP_OUT_UINT8 = 5,          /* uint8 codes with offset 128: rint(y) + 128 clamped to [0, 255], [rows, cols] */
   EP_OUT_LATTICE2X_I32 = 100 /* int32 2*x_i (exact lattice coordinates), for tests */
 } ep_out_dtype;
 
@@ -104,7 +107,14 @@ typedef struct {
   int32_t min_offset[EP_NUM_TABLES];  /* value of symbol 0 of table k (min_offset[0] == 0);
                                          -2^19 <= min_offset[k] and min_offset[k] + A_k <= 2^19,
                                          which keeps every reconstructed 4z + c exact in fp32 */
+  uint32_t field8;                    /* EP_FIELD8_M (0): field 8 is m = floor(z8 / 2), the
+                                         method's parity-reduced field; EP_FIELD8_Z8 (1): field 8
+                                         is z8 itself (the direct-z8 ablation of the paper's
+                                         Table 4); other values are rejected */
 } ep_tensor_desc;
+
+#define EP_FIELD8_M 0u
+#define EP_FIELD8_Z8 1u
 
 /* Human-readable name of a status code (static string). */
 const char* ep_status_string(int status);

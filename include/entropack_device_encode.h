@@ -43,16 +43,19 @@ int ep_encode_device_workspace_size(int64_t rows, int64_t cols, double target_bp
 /*
  * Compress the device float32 matrix W [rows, cols] (row-major, 16-byte
  * aligned, cols % 8 == 0).  target_bpp, vectors_per_tile, prob_bits and
- * route mean what they mean for ep_encode_host.  workspace: device buffer of
- * at least ep_encode_device_workspace_size() bytes, 256-byte aligned; it holds
+ * route mean what they mean for ep_encode_host; coding is an ep_coding (the
+ * ablations reuse the standard coding's scale, points and row scales; an
+ * ablation whose alphabet outgrows 2^b returns EP_ERR_UNSUPPORTED).
+ * workspace: device buffer of at least ep_encode_device_workspace_size()
+ * bytes, 256-byte aligned; it holds
  * the encoded arrays afterwards.  The call enqueues its kernels on `stream`
  * (a hipStream_t) and synchronises that stream several times: it returns when
  * the tensor is encoded, with the header written to *info.  A later call on
  * the same workspace overwrites the result.
  */
 int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_bpp,
-                     uint32_t vectors_per_tile, uint32_t prob_bits, int route, void* workspace,
-                     size_t ws_bytes, void* stream, ep_encoded_info* info);
+                     uint32_t vectors_per_tile, uint32_t prob_bits, int route, int coding,
+                     void* workspace, size_t ws_bytes, void* stream, ep_encoded_info* info);
 
 /*
  * Copy the result of the last ep_encode_device on `workspace` (described by

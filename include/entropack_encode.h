@@ -28,6 +28,13 @@ extern "C" {
 
 typedef enum { EP_ROUTE_DIRECT = 0, EP_ROUTE_FP8 = 1, EP_ROUTE_INT8 = 2 } ep_route;
 
+/* Field coding: the method's (17 coset-conditioned tables, m = floor(z8/2) as
+ * the eighth field) and the two ablations of the paper's Table 4, which keep
+ * the method's quantised points and row scales.  A pooled container lists the
+ * shared table under both cosets (equal freq_base, alphabet and min_offset);
+ * a direct-z8 container is decoded with ep_tensor_desc.field8 = EP_FIELD8_Z8. */
+typedef enum { EP_CODING_STANDARD = 0, EP_CODING_POOLED = 1, EP_CODING_DIRECT_Z8 = 2 } ep_coding;
+
 typedef struct ep_encoded ep_encoded;
 
 typedef struct {
@@ -42,6 +49,7 @@ typedef struct {
   uint32_t alphabet[17];
   int32_t min_offset[17];
   uint32_t freq_base[17];
+  int32_t coding;              /* ep_coding (the host compressor always writes EP_CODING_STANDARD) */
 } ep_encoded_info;
 
 /*

@@ -98,6 +98,7 @@ def test_workspace_size_of_valid_descriptors():
     (lambda d: d.min_offset.__setitem__(3, -(1 << 20)), "2^19"),
     (lambda d: setattr(d, "payload", 0x1002), "aligned"),
     (lambda d: setattr(d, "freqs", None), "NULL"),
+    (lambda d: setattr(d, "field8", 2), "field8"),
 ])
 def test_malformed_descriptors_are_rejected(mutate, needle):
     d = _desc()
@@ -167,18 +168,20 @@ def test_device_encoder_workspace_size_and_argument_errors():
     info = enc.EncodedInfo()
     fake = C.c_void_p(1 << 40)
     ws_need = ep.encode_device_workspace_size(8, 64, 4.0)
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, fake, ws_need, None, None) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_encode_device(None, 8, 64, 4.0, 0, 0, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_encode_device(C.c_void_p((1 << 40) + 4), 8, 64, 4.0, 0, 0, 0, fake, ws_need, None,
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, 0, fake, ws_need, None, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(None, 8, 64, 4.0, 0, 0, 0, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(C.c_void_p((1 << 40) + 4), 8, 64, 4.0, 0, 0, 0, 0, fake, ws_need, None,
                               C.byref(info)) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 8, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 16, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, fake, ws_need - 1, None,
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 8, 0, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 16, 0, 0, fake, ws_need, None, C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, 0, fake, ws_need - 1, None,
                               C.byref(info)) == ep.EP_ERR_WORKSPACE
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, None, ws_need, None, C.byref(info)) == ep.EP_ERR_WORKSPACE
-    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, C.c_void_p((1 << 40) + 128), ws_need, None,
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, 0, None, ws_need, None, C.byref(info)) == ep.EP_ERR_WORKSPACE
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, 0, C.c_void_p((1 << 40) + 128), ws_need, None,
                               C.byref(info)) == ep.EP_ERR_INVALID_ARG
     assert b"aligned" in L.ep_last_error()
+    assert L.ep_encode_device(fake, 8, 64, 4.0, 0, 0, 0, 3, fake, ws_need, None,
+                              C.byref(info)) == ep.EP_ERR_INVALID_ARG
     # emit rejects a header that does not describe an encoded tensor
     info.rows, info.cols, info.vectors_per_tile, info.num_tiles = 8, 64, 32, 99
     assert L.ep_encode_device_emit(fake, C.byref(info), None, None, None, None, None, None,

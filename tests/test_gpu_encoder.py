@@ -163,3 +163,18 @@ def test_device_encoder_full_reference_layer(route):
     _assert_same_container(ref, d, f"reference layer {route}")
     assert d.est_bpp == ref.est_bpp
     _decode_ok(d, "bf16" if route == "direct" else "fp8")
+
+
+@pytest.mark.parametrize("coding", ["pooled", "direct_z8"])
+@pytest.mark.parametrize("target", [2.0, 4.0, 8.0])
+def test_device_encoder_table4_codings(coding, target):
+    # the two ablations of the paper's Table 4: same points and scales, other tables
+    W = synthgen.student_t_weights(256, 1024, 31, bf16=True).numpy()
+    print(f"[device encoder] {coding} target={target}", flush=True)
+    ref = oracle.encode(W, target, coding=coding)
+    d = ep.encode_device(torch.from_numpy(W).cuda(), target, coding=coding)
+    _assert_same_container(ref, d, f"{coding} {target}")
+    assert d.packed.field8 == (1 if coding == "direct_z8" else 0)
+    out = _decode_ok(d, "lattice2x")
+    std = oracle.encode(W, target)
+    assert np.array_equal(out.cpu().numpy(), oracle.decode(std, "lattice2x")[0])

@@ -60,7 +60,7 @@ def test_library_exports_and_version():
     L = ep.lib()
     for name in ep.EXPORTS:
         assert hasattr(L, name)
-    assert L.ep_abi_version() == 2
+    assert L.ep_abi_version() == 3
 
 
 @pytest.mark.parametrize("V", [512, 455])
@@ -88,7 +88,7 @@ def test_routes_fp8_and_int8_codes():
     ct8 = oracle.encode(W, 5.0, route="fp8")
     _check_parity(ct8, kinds=("fp8", "lattice2x", "bf16"), label="fp8 route")
     cti = oracle.encode(W, 8.0, route="int8")
-    _check_parity(cti, kinds=("int8", "lattice2x"), label="int8 route 8bpp")
+    _check_parity(cti, kinds=("int8", "uint8", "lattice2x"), label="int8 route 8bpp")
     cti2 = oracle.encode(W, 2.0, route="int8")
     _check_parity(cti2, kinds=("int8",), label="int8 route 2bpp")
 
@@ -97,7 +97,7 @@ def test_int8_and_fp8_saturation_paths():
     # decoding a direct-route tensor into INT8 / FP8 exercises clamping and subnormals
     W = (synthgen.student_t_weights(64, 512, 7).numpy() * 4000.0).astype(np.float32)
     ct = oracle.encode(W, 6.0)
-    _check_parity(ct, kinds=("int8", "fp8"), label="saturation")
+    _check_parity(ct, kinds=("int8", "uint8", "fp8"), label="saturation")
     Ws = (synthgen.student_t_weights(64, 512, 8).numpy() * 1e-2).astype(np.float32)
     cts = oracle.encode(Ws, 6.0)
     _check_parity(cts, kinds=("fp8",), label="fp8 subnormals")
@@ -135,7 +135,8 @@ def test_batch_mixed_tensors_one_call():
         tgt = float(rng.choice([2.0, 4.0, 8.0]))
         route = ["direct", "fp8", "int8"][i % 3]
         cts.append(oracle.encode(W, tgt, V=int(rng.integers(32, 500)), route=route))
-        kinds.append({"direct": ["bf16", "fp16", "fp32"][i % 9 // 3], "fp8": "fp8", "int8": "int8"}[route])
+        kinds.append({"direct": ["bf16", "fp16", "fp32"][i % 9 // 3], "fp8": "fp8",
+                      "int8": ["int8", "uint8"][i // 3 % 2]}[route])
     # an empty tensor in the middle of the batch
     cts.insert(3, oracle.encode(np.zeros((0, 64), np.float32), 4.0))
     kinds.insert(3, "bf16")
@@ -229,7 +230,7 @@ def test_wide_alphabets(b, s, lo, hi):
     W = synthgen.student_t_weights(64, 1024, 11 + b, outlier_frac=0.002).numpy()
     ct = oracle.encode_fixed_scale(W, s, V=96, b=b)
     assert lo <= int(ct.alphabet[1:].max()) <= hi
-    _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8"), label=f"b={b} A={ct.alphabet[1:].max()}")
+    _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8", "uint8"), label=f"b={b} A={ct.alphabet[1:].max()}")
 
 
 @pytest.mark.parametrize("rows, cols, V", [
@@ -252,3 +253,17 @@ def test_tensor_smaller_than_one_round():
     ct = oracle.encode_fixed_scale(W, 0.1, V=32, b=11)
     assert ct.T == 1 and ct.rows * ct.cols // 8 < 32
     _check_parity(ct, kinds=("bf16", "lattice2x", "fp32"), label="16 vectors")
+
+
+@pytest.mark.parametrize("coding", ["pooled", "direct_z8"])
+@pytest.mark.parametrize("target, b", [(4.0, 11), (4.0, 9), (4.0, 10), (7.0, 11), (4.0, 12), (8.0, 13)])
+def test_table4_coding_variants(coding, target, b):
+    # the two ablations of the paper's Table 4 through every table layout: pooled
+    # tables share one frequency table per field between the cosets; direct z8
+    # sets the descriptor's field8 flag
+    W = synthgen.student_t_weights(160, 1024, 70 + b, bf16=True).numpy()
+    ct = oracle.encode(W, target, b=b, coding=coding)
+    print(f"[table4] {coding} target={target} b={ct.b} A={ct.alphabet[1:].max()}", flush=True)
+    _check_parity(ct, kinds=("lattice2x", "bf16", "int8"), label=f"{coding} b={ct.b}")
+    std = oracle.encode(W, target, b=b)
+    assert np.array_equal(oracle.decode(std, "lattice2x")[0], oracle.decode(ct, "lattice2x")[0])
