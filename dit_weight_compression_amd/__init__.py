@@ -24,7 +24,8 @@ TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1,
 
 # every symbol include/entropack.h declares
 EXPORTS = ["ep_status_string", "ep_last_error", "ep_abi_version", "ep_workspace_size",
-           "ep_decode_batch", "ep_decode_tensor", "ep_batch_prepare", "ep_batch_launch"]
+           "ep_decode_batch", "ep_decode_tensor", "ep_batch_prepare", "ep_batch_launch",
+           "ep_convert_f32"]
 # every symbol include/entropack_device_encode.h declares (same library)
 DEVICE_ENCODE_EXPORTS = ["ep_encode_device_workspace_size", "ep_encode_device",
                          "ep_encode_device_emit"]
@@ -90,6 +91,8 @@ def lib():
         L.ep_batch_prepare.restype = C.c_int
         L.ep_batch_launch.argtypes = [vp, vp]
         L.ep_batch_launch.restype = C.c_int
+        L.ep_convert_f32.argtypes = [vp, vp, C.c_uint64, C.c_int, vp]
+        L.ep_convert_f32.restype = C.c_int
         L.ep_encode_device_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_uint32,
                                                       C.c_int, C.POINTER(C.c_size_t)]
         L.ep_encode_device_workspace_size.restype = C.c_int
@@ -351,3 +354,20 @@ def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "di
 
 ep_encode_device = encode_device
 ep_encode_device_workspace_size = encode_device_workspace_size
+
+
+def convert_f32(y, dtype: str, stream=None):
+    """Container rounding of a float32 device tensor (ep_convert_f32); returns the codes."""
+    torch = _torch()
+    y = y.contiguous()
+    if y.dtype != torch.float32 or not y.is_cuda or y.numel() % 4:
+        raise ValueError("y must be a float32 device tensor with a multiple of 4 elements")
+    out = torch.empty(y.shape, dtype=torch_dtype(dtype), device=y.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    _check(lib().ep_convert_f32(y.data_ptr(), out.data_ptr(), y.numel(), DTYPES[dtype],
+                                C.c_void_p(stream.cuda_stream)))
+    return out
+
+
+ep_convert_f32 = convert_f32

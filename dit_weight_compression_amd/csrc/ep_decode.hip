@@ -232,24 +232,21 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
 }
 
 // ---------------------------------------------------------------- container rounding
-// OCP e4m3fn: clamp to +-448, then round to nearest even at the format's quantum.
-__device__ __forceinline__ uint32_t fp8_e4m3_rne(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  float a = fminf(fabsf(y), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                        // below 2^-6: subnormal quantum 2^-9
-    code = uint32_t(__builtin_rintf(a * 512.0f));
-  } else {
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);         // keep 3 mantissa bits, ties to even
-    code = (u >> 20) - (120u << 3);           // rebias the exponent from 127 to 7
-  }
-  return sign | code;
+// OCP e4m3fn codes of four values, bytes in order: clamp to +-448 (v_med3_f32),
+// then gfx950's conversion to OCP FP8 (round to nearest even, subnormals and
+// signed zeros kept), two values per instruction.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi), __builtin_amdgcn_fmed3f(b, lo, hi),
+                                          0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi), __builtin_amdgcn_fmed3f(d, lo, hi), w,
+                                      true);
+  return uint32_t(w);
 }
 
+// INT8 code: round half to even, clamp to [-128, 127] (v_med3_f32).
 __device__ __forceinline__ uint32_t int8_rne(float y) {
-  float r = __builtin_rintf(y);
-  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(y), -128.0f, 127.0f);
   return uint32_t(int32_t(r)) & 0xFFu;
 }
 
@@ -569,10 +566,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         __builtin_amdgcn_raw_buffer_store_b128(lo, rO, ob, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(hi, rO, ob + 16u, 0, 0);
       } else if (OK == kOutFP8) {
-        const u32x2 w = {fp8_e4m3_rne(y[0]) | (fp8_e4m3_rne(y[1]) << 8) | (fp8_e4m3_rne(y[2]) << 16) |
-                             (fp8_e4m3_rne(y[3]) << 24),
-                         fp8_e4m3_rne(y[4]) | (fp8_e4m3_rne(y[5]) << 8) | (fp8_e4m3_rne(y[6]) << 16) |
-                             (fp8_e4m3_rne(y[7]) << 24)};
+        const u32x2 w = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       } else {
         // INT8 codes; UINT8 adds the offset 128, i.e. flips each byte's top bit
@@ -641,6 +635,28 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     }
     cur = ch.tensor;
     decode_pair<BT, TL, OK>(T, ch.tile0, tiles_per_chunk, smem, ring);
+  }
+}
+
+// Container rounding of n4 groups of four fp32 values with the decode
+// kernel's own conversions (ep_convert_f32).
+template <int OK>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ in, void* __restrict__ out,
+                                                     uint64_t n4) {
+  for (uint64_t q = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n4;
+       q += uint64_t(gridDim.x) * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(in)[q];
+    if (OK == kOutBF16) {
+      reinterpret_cast<u32x2*>(out)[q] = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    } else if (OK == kOutFP16) {
+      reinterpret_cast<u32x2*>(out)[q] = u32x2{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)};
+    } else if (OK == kOutFP8) {
+      reinterpret_cast<uint32_t*>(out)[q] = pack_fp8x4(v.x, v.y, v.z, v.w);
+    } else {
+      const uint32_t off = OK == kOutUINT8 ? 0x80808080u : 0u;
+      reinterpret_cast<uint32_t*>(out)[q] =
+          (int8_rne(v.x) | (int8_rne(v.y) << 8) | (int8_rne(v.z) << 16) | (int8_rne(v.w) << 24)) ^ off;
+    }
   }
 }
 
@@ -1013,6 +1029,27 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
   void* outs[1] = {out};
   int32_t* sts[1] = {tile_status};
   return ep_decode_batch(desc, &dtype, outs, sts, 1, workspace, ws_bytes, stream);
+}
+
+int ep_convert_f32(const float* in, void* out, uint64_t n, int dtype, void* stream) {
+  if (n % 4 != 0) return fail(EP_ERR_INVALID_ARG, "n must be a multiple of 4");
+  if (n == 0) return EP_OK;
+  if (!in || !out || reinterpret_cast<uintptr_t>(in) % 16 || reinterpret_cast<uintptr_t>(out) % 8)
+    return fail(EP_ERR_INVALID_ARG, "in must be 16-byte and out 8-byte aligned device pointers");
+  const uint64_t n4 = n / 4;
+  const dim3 grid(uint32_t(std::min<uint64_t>((n4 + 255) / 256, 1u << 16)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case EP_OUT_BF16: hipLaunchKernelGGL(convert_kernel<kOutBF16>, grid, dim3(256), 0, st, in, out, n4); break;
+    case EP_OUT_FP16: hipLaunchKernelGGL(convert_kernel<kOutFP16>, grid, dim3(256), 0, st, in, out, n4); break;
+    case EP_OUT_FP8_E4M3: hipLaunchKernelGGL(convert_kernel<kOutFP8>, grid, dim3(256), 0, st, in, out, n4); break;
+    case EP_OUT_INT8: hipLaunchKernelGGL(convert_kernel<kOutINT8>, grid, dim3(256), 0, st, in, out, n4); break;
+    case EP_OUT_UINT8: hipLaunchKernelGGL(convert_kernel<kOutUINT8>, grid, dim3(256), 0, st, in, out, n4); break;
+    default: return fail(EP_ERR_INVALID_ARG, "dtype must be BF16, FP16, FP8_E4M3, INT8 or UINT8");
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("convert launch: ") + hipGetErrorString(e));
+  return EP_OK;
 }
 
 }  // extern "C"

@@ -164,6 +164,18 @@ typedef struct {
   uint64_t opaque[128];
 } ep_batch_plan;
 
+/*
+ * Container rounding on its own: out[i] = the dtype's code of the fp32 value
+ * in[i], computed with the decode kernel's device conversions (the rules at
+ * the top of this file), for callers that hold fp32 products and for testing
+ * the rounding in isolation.  in: device float32 [n], 16-byte aligned; out:
+ * device [n] of the dtype's element (BF16 / FP16 uint16 bit patterns, FP8 /
+ * INT8 / UINT8 bytes), 8-byte aligned; n a multiple of 4.  dtype is one of
+ * EP_OUT_BF16, EP_OUT_FP16, EP_OUT_FP8_E4M3, EP_OUT_INT8, EP_OUT_UINT8.
+ * Enqueued on `stream`.
+ */
+int ep_convert_f32(const float* in, void* out, uint64_t n, int dtype, void* stream);
+
 int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const* outs,
                      int32_t* const* tile_status, int n, void* workspace, size_t ws_bytes,
                      void* stream, ep_batch_plan* plan);

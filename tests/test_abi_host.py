@@ -186,3 +186,16 @@ def test_device_encoder_workspace_size_and_argument_errors():
     info.rows, info.cols, info.vectors_per_tile, info.num_tiles = 8, 64, 32, 99
     assert L.ep_encode_device_emit(fake, C.byref(info), None, None, None, None, None, None,
                                    None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_convert_argument_errors():
+    import ctypes as C
+    L = ep.lib()
+    fake = C.c_void_p(1 << 40)
+    assert L.ep_convert_f32(fake, fake, 6, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_convert_f32(None, fake, 8, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_convert_f32(C.c_void_p((1 << 40) + 8), fake, 8, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_convert_f32(fake, C.c_void_p((1 << 40) + 4), 8, 0, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_convert_f32(fake, fake, 8, 100, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_convert_f32(fake, fake, 8, 4, None) == ep.EP_ERR_INVALID_ARG   # FP32 needs no rounding
+    assert L.ep_convert_f32(fake, fake, 0, 0, None) == ep.EP_OK

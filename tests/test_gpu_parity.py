@@ -267,3 +267,44 @@ def test_table4_coding_variants(coding, target, b):
     _check_parity(ct, kinds=("lattice2x", "bf16", "int8"), label=f"{coding} b={ct.b}")
     std = oracle.encode(W, target, b=b)
     assert np.array_equal(oracle.decode(std, "lattice2x")[0], oracle.decode(ct, "lattice2x")[0])
+
+
+def _rounding_probe_values() -> np.ndarray:
+    # every exponent of 2^-30 .. 2^16 (FP8 and FP16 subnormals to FP16 overflow) with
+    # all 128 patterns of the top 7 mantissa bits and low bits at the BF16 (bit 15),
+    # FP16 (bit 12) and FP8 (bit 19, inside the top bits) ties and next to them
+    lows = np.array([0, 1, 0x0FFF, 0x1000, 0x1001, 0x3000, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    exps = np.arange(127 - 30, 127 + 17, dtype=np.uint32)
+    hi = np.arange(128, dtype=np.uint32) << 16
+    bits = (exps[:, None, None] << 23) | hi[None, :, None] | lows[None, None, :]
+    bits = bits.reshape(-1)
+    vals = np.concatenate([bits, bits | 0x80000000]).view(np.float32)
+    halves = np.arange(-261, 262, dtype=np.float32) * np.float32(0.5)          # INT8 ties and limits
+    near = np.concatenate([np.nextafter(halves, np.float32(np.inf)), np.nextafter(halves, np.float32(-np.inf))])
+    special = np.float32([0.0, -0.0, 448.0, -448.0, 464.0, -464.0, 480.0, 1e30, -1e30, 65504.0, 65520.0,
+                          -65520.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 1e-45, -1e-45, 1.17549435e-38])
+    rng = np.random.default_rng(17)
+    uni = rng.uniform(-500, 500, 1 << 20).astype(np.float32)
+    rb = (rng.integers(90, 150, 1 << 18, dtype=np.uint32) << 23) | rng.integers(0, 1 << 23, 1 << 18, dtype=np.uint32)
+    rb |= rng.integers(0, 2, 1 << 18, dtype=np.uint32) << 31
+    v = np.concatenate([vals, halves, near, special, uni, rb.view(np.float32)])
+    pad = (-v.size) % 4
+    return np.concatenate([v, np.zeros(pad, np.float32)])
+
+
+def test_container_rounding_matches_oracle_at_every_boundary():
+    # ep_convert_f32 runs the decode kernel's own conversion code (FP8 through the
+    # hardware v_cvt_pk_fp8_f32 after a v_med3 clamp)
+    v = _rounding_probe_values()
+    y = torch.from_numpy(v).cuda()
+    refs = {"bf16": oracle.f32_to_bf16(v), "fp16": oracle.f32_to_fp16(v), "fp8": oracle.f32_to_fp8(v),
+            "int8": oracle.f32_to_int8(v), "uint8": oracle.f32_to_uint8(v)}
+    for kind, ref in refs.items():
+        got = _gpu_out_numpy(ep.convert_f32(y, kind), kind)
+        torch.cuda.synchronize()
+        ref = np.asarray(ref).view(got.dtype)
+        if not np.array_equal(got, ref):
+            bad = np.flatnonzero(got != ref)
+            i = bad[0]
+            raise AssertionError(f"{kind}: {bad.size} of {v.size} differ; first y={v[i]!r} "
+                                 f"(bits {v[i:i+1].view(np.uint32)[0]:#010x}) gpu={got[i]} oracle={ref[i]}")
