@@ -61,7 +61,7 @@ class EpTensorDesc(C.Structure):
 
 
 class EpBatchPlan(C.Structure):
-    _fields_ = [("opaque", C.c_uint64 * 128)]
+    _fields_ = [("opaque", C.c_uint64 * 256)]
 
 
 _lib = None

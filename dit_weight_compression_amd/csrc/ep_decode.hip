@@ -57,21 +57,33 @@ constexpr size_t kMaxLds = 160 * 1024;
 //             the float value 2 z + c (4 m + c for m), at stride 256.
 //   workspace (anything else): the narrow scheme with u16 slot maps and stride
 //             2^b, read from the workspace through the caches.
-enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2, kTabPackedWide = 3 };
-enum Variant : uint32_t { kVarP9 = 0, kVarP10, kVarP11, kVarW10, kVarW11, kVarN12, kVarWs, kNumVariants };
+//   hybrid    (b = 11, 12 with alphabets too large for the above): the
+//             workspace format, with the u16 slot maps (64 / 128 KB) staged in
+//             LDS and the per-symbol entries read through the caches.
+enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2, kTabPackedWide = 3, kTabHybrid = 4 };
+enum Variant : uint32_t {
+  kVarP9 = 0, kVarP10, kVarP11, kVarW10, kVarW11, kVarN12, kVarH11, kVarH12, kVarWs, kNumVariants
+};
 
 __host__ __device__ constexpr int layout_of(uint32_t v) {
-  return v <= kVarP11 ? kTabPacked : v <= kVarW11 ? kTabPackedWide : v == kVarN12 ? kTabNarrow : kTabWorkspace;
+  return v <= kVarP11 ? kTabPacked : v <= kVarW11 ? kTabPackedWide : v == kVarN12 ? kTabNarrow
+       : v <= kVarH12 ? kTabHybrid : kTabWorkspace;
 }
+// format of the table block the build writes (the hybrid layout reuses the workspace format)
+__host__ __device__ constexpr int storage_of(int tl) { return tl == kTabHybrid ? kTabWorkspace : tl; }
 __host__ __device__ constexpr bool is_packed(int tl) { return tl == kTabPacked || tl == kTabPackedWide; }
 __host__ __device__ constexpr uint32_t stride_of(int tl, uint32_t b) {
-  return tl == kTabNarrow ? 256u : tl == kTabWorkspace ? (1u << b) : 0u;
+  return tl == kTabNarrow ? 256u : (tl == kTabWorkspace || tl == kTabHybrid) ? (1u << b) : 0u;
 }
 __host__ __device__ constexpr size_t lut_bytes_of(int tl, uint32_t b) {
   return (size_t(16) << b) * (is_packed(tl) ? 4 : tl == kTabNarrow ? 1 : 2);
 }
 __host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
   return lut_bytes_of(tl, b) + 2 * size_t(16) * stride_of(tl, b) * 4;
+}
+// bytes of a tensor's tables that the decode kernel stages in LDS
+__host__ __device__ constexpr size_t lds_table_bytes_of(int tl, uint32_t b) {
+  return tl == kTabWorkspace ? 0 : tl == kTabHybrid ? lut_bytes_of(tl, b) : table_bytes_of(tl, b);
 }
 
 // Device-side view of one tensor (lives in the workspace).
@@ -155,7 +167,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   const uint32_t A = T.alphabet[k];
   const uint32_t b = T.b;
   const uint32_t M = 1u << b;
-  const int tl = layout_of(T.variant);
+  const int tl = storage_of(layout_of(T.variant));
   const uint32_t S = stride_of(tl, b);
   unsigned char* lut8 = T.tab + (size_t(t) << b);
   uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
@@ -306,10 +318,12 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
                                             const unsigned char* __restrict__ lds,
                                             uint16_t* __restrict__ ring) {
   constexpr bool kWs = TL == kTabWorkspace;
+  constexpr bool kHyb = TL == kTabHybrid;
+  constexpr bool kGlobalEntries = kWs || kHyb;             // per-symbol entries read from the workspace
   const uint32_t B = BT ? uint32_t(BT) : T.b;
   const uint32_t M = 1u << B;
   const uint32_t MASK = M - 1u;
-  const uint32_t S = kWs ? M : 256u;                        // sym / val stride (narrow, workspace)
+  const uint32_t S = kGlobalEntries ? M : 256u;             // sym / val stride (narrow, workspace, hybrid)
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t half = lane >> 5;
   const uint32_t hs = half << 4;                            // selects this half's packed 16 bits
@@ -363,7 +377,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t sh8 = T.f8z8 ? 1u : 2u;
   const uint32_t empty = T.empty_mask;
   const bool slow_rows = T.slow_rows != 0;
-  const unsigned char* tbase = kWs ? T.tab : lds;
+  const unsigned char* tbase = kGlobalEntries ? T.tab : lds;
   const uint32_t lut_bytes = uint32_t(lut_bytes_of(TL, B));
   // packed tables: fields 5..8 of b = 11 lie beyond the 16-bit LDS offset of
   // the lookup instruction, so they get a second coset base
@@ -515,13 +529,14 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         const uint32_t addr = (x & MASK) | lb;           // slot + coset * 2^b
         uint32_t s;
         if (kWs) s = reinterpret_cast<const uint16_t*>(tbase)[(uint32_t(2 * (f - 1)) << B) + addr];
+        else if (kHyb) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr];
         else s = lds[(uint32_t(2 * (f - 1)) << B) + addr];
         const uint32_t eo = cb + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
         const uint32_t e = *reinterpret_cast<const uint32_t*>(tbase + eo);
         vv[f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
         q = x >> B;
-        x = __umul24(e & (kWs ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
-        sv[f] = kWs ? s : e;
+        x = __umul24(e & (kGlobalEntries ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
+        sv[f] = kGlobalEntries ? s : e;
         EP_RENORM();
       }
       const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(sv[1], sv[2], sv[3], 0x96),
@@ -615,7 +630,7 @@ template <int BT, int TL, int OK>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
                                                         const Chunk* __restrict__ chunks,
                                                         uint32_t nchunks, uint32_t tiles_per_chunk) {
-  constexpr size_t kTab = TL == kTabWorkspace ? 0 : table_bytes_of(TL, BT);
+  constexpr size_t kTab = lds_table_bytes_of(TL, BT);
   __shared__ __align__(16) unsigned char smem[kTab + kRingBytes];
   const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
   const uint32_t c0 = blockIdx.x * per;
@@ -630,7 +645,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       __syncthreads();
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)T.tab;
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
-      for (uint32_t i = threadIdx.x; i < T.tab_bytes / 16u; i += kBlock) dst[i] = src[i];
+      for (uint32_t i = threadIdx.x; i < uint32_t(kTab / 16u); i += kBlock) dst[i] = src[i];
       __syncthreads();
     }
     cur = ch.tensor;
@@ -674,6 +689,8 @@ uint32_t choose_variant(const ep_tensor_desc& d) {
     return kVarW10 + (d.prob_bits - 10);
   if (d.prob_bits == 12 && amax <= 256 && table_bytes_of(kTabNarrow, 12) + kRingBytes <= kMaxLds)
     return kVarN12;
+  if ((d.prob_bits == 11 || d.prob_bits == 12) && lds_table_bytes_of(kTabHybrid, d.prob_bits) + kRingBytes <= kMaxLds)
+    return kVarH11 + (d.prob_bits - 11);
   return kVarWs;
 }
 
@@ -783,7 +800,7 @@ struct PlanImpl {
   Group groups[kNumGroups];
 };
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
-constexpr uint64_t kPlanMagic = 0x45504c414e763034ull;
+constexpr uint64_t kPlanMagic = 0x45504c414e763035ull;
 
 using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t, uint32_t);
 
@@ -809,6 +826,8 @@ KernelFn kernel_of(uint32_t group) {
     case kVarW10: return kernel_for_kind<10, kTabPackedWide>(ok);
     case kVarW11: return kernel_for_kind<11, kTabPackedWide>(ok);
     case kVarN12: return kernel_for_kind<12, kTabNarrow>(ok);
+    case kVarH11: return kernel_for_kind<11, kTabHybrid>(ok);
+    case kVarH12: return kernel_for_kind<12, kTabHybrid>(ok);
     default: return kernel_for_kind<0, kTabWorkspace>(ok);
   }
 }

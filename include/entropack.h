@@ -161,7 +161,7 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
  * workspace.
  */
 typedef struct {
-  uint64_t opaque[128];
+  uint64_t opaque[256];
 } ep_batch_plan;
 
 /*

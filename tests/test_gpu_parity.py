@@ -308,3 +308,16 @@ def test_container_rounding_matches_oracle_at_every_boundary():
             i = bad[0]
             raise AssertionError(f"{kind}: {bad.size} of {v.size} differ; first y={v[i]!r} "
                                  f"(bits {v[i:i+1].view(np.uint32)[0]:#010x}) gpu={got[i]} oracle={ref[i]}")
+
+
+@pytest.mark.parametrize("target, b, outliers", [(7.0, 11, 0.002), (8.0, 12, 0.0), (7.0, 12, 0.0)])
+def test_hybrid_layout_large_alphabets(target, b, outliers):
+    # b = 11 with alphabets above 1024 and b = 12 above 256: the u16 slot maps sit
+    # in LDS, the per-symbol entries are read from the workspace
+    W = synthgen.student_t_weights(192, 2048, 101 if b == 11 else 90 + b, bf16=True,
+                                   outlier_frac=outliers).numpy()
+    ct = oracle.encode(W, target, b=b)
+    amax = int(ct.alphabet[1:].max())
+    print(f"[hybrid] target={target} b={ct.b} A={amax}", flush=True)
+    assert ct.b == b and amax > (1024 if b == 11 else 256)
+    _check_parity(ct, kinds=("lattice2x", "bf16", "fp8", "uint8"), label=f"hybrid b={b} A={amax}")
