@@ -13,6 +13,15 @@
  * side follows the stored FP32 scales: g = fp32(s * r_row), y = fp32(x * g),
  * then BF16 / FP8-e4m3 / INT8 rounding as documented in epo_convert.c.
  *
+ * Pins (tests/test_oracle_*.py, tests/golden/): brute force and the E8
+ * constants for the lattice, round trips and code-length bounds for rANS,
+ * Table 5's tile accounting and Table 4's rate effects, closed forms for the
+ * row statistics and the refit, library casts for every container rounding.
+ * Parity unpinned against the pages (they print no stream bytes, scales,
+ * samples or estimates): the E8 tie-breaks, the frequency normalisation rule,
+ * the scale search's row sample and rate estimator, and the byte layout; each
+ * is pinned only by its invariants.
+ *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared.
  */
 #ifndef EPO_H

@@ -341,6 +341,12 @@ static int finish_encode(const float* Wq, int64_t rows, int64_t cols, float s, u
   for (int k = 0; k < EPO_TABLES; ++k)
     if (!has[k]) t->minval[k] = 0;
   t->minval[0] = 0;
+  /* an ablation's alphabets (z8, or a pooled range) may outgrow 2^b */
+  for (int k = 1; k < EPO_TABLES; ++k)
+    if (t->alphabet[k] > (1u << b)) {
+      free(zf);
+      return -13;
+    }
   uint64_t** counts = table_counts(fields, nvec, t->minval, t->alphabet);
   if (coding == EPO_CODING_POOLED) {
     /* pooled counts; the coset-1 slot shares the coset-0 table */

@@ -160,9 +160,16 @@ def test_deterministic_repeat_and_workspace_reuse():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_corrupt_streams_flagged_like_oracle():
-    W = synthgen.student_t_weights(64, 512, 11).numpy()
-    ct = oracle.encode(W, 4.0, V=64)
+@pytest.mark.parametrize("target, b, outliers, rows, cols", [
+    (4.0, 11, 0.0, 64, 512),        # packed tables
+    (4.0, 12, 0.0, 64, 512),        # narrow tables
+    (8.0, 12, 0.002, 96, 2048),     # hybrid tables (A > 256 at b = 12)
+    (8.0, 13, 0.002, 96, 2048),     # global tables
+])
+def test_corrupt_streams_flagged_like_oracle(target, b, outliers, rows, cols):
+    W = synthgen.student_t_weights(rows, cols, 11, outlier_frac=outliers).numpy()
+    ct = oracle.encode(W, target, V=64, b=b)
+    print(f"[corrupt] b={ct.b} A={ct.alphabet[1:].max()} T={ct.T}", flush=True)
     rng = np.random.default_rng(0)
     pl = ct.payload.copy()
     stt = ct.states.copy()

@@ -159,6 +159,11 @@ def test_row_refit_is_least_squares():
         num = (W[r].astype(np.float64) * X[r]).sum()
         den = (X[r] ** 2).sum()
         assert ct.row_scales[r] == np.float32(num / den)
+    # least squares: the residual is orthogonal to the row's points (normal equation), up to
+    # the rounding of the stored fp32 scale
+    for r in range(W.shape[0]):
+        resid = W[r].astype(np.float64) - np.float64(ct.row_scales[r]) * X[r]
+        assert abs((resid * X[r]).sum()) <= 1e-6 * (X[r] ** 2).sum() * abs(np.float64(ct.row_scales[r])) + 1e-12
     # the fitted scale does at least as well as the row RMS it started from
     n = np.sqrt((W.astype(np.float64) ** 2).mean(axis=1))
     fit = ((W - ct.row_scales[:, None] * X) ** 2).sum()

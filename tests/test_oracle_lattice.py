@@ -188,3 +188,9 @@ def test_row_rms():
     n = oracle.row_rms(W)
     assert n[0] == pytest.approx(np.sqrt(25.0 / 8.0), rel=1e-15)
     assert n[1] == 0.0
+    # closed forms of the root-mean-square (not the standard deviation, not the mean |w|):
+    # a constant row has RMS |a|; a lone nonzero a among 16 columns has RMS |a| / 4
+    V = np.zeros((2, 16), np.float32)
+    V[0, :] = -2.5
+    V[1, 5] = 6.0
+    assert list(oracle.row_rms(V)) == [2.5, 1.5]
