@@ -99,11 +99,11 @@ struct alignas(16) DevTensor {
   uint32_t tab_bytes;        // bytes of the table block
   uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
   uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
-  uint32_t slow_rows;        // set by the table build: rowv holds g, not g/2
+  uint32_t slow_rows;        // set by the table build when some row's g/2 is inexact: use g
   uint32_t f8z8;             // 1: field 8 holds z8 (no parity reduction), 0: it holds m
   uint64_t payload_words;
   const float* row_scales;
-  float* rowv;               // workspace: per-row multiplier g/2 (or g), g = fp32(scale * row scale)
+  float* rowv;               // workspace: per row the pair (g/2, g), g = fp32(scale * row scale)
   const uint32_t* states;
   const uint32_t* offsets;
   const uint16_t* payload;
@@ -141,23 +141,23 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens) {
   DevTensor& T = tens[blockIdx.y];
   if (T.T == 0) return;
-  if (blockIdx.x == 16) {
-    // per-row multipliers.  (2 z + c) * (g / 2) equals (z + c/2) * g exactly
-    // whenever g / 2 is exact; a tensor with any row where it is not keeps g.
-    __shared__ uint32_t inexact;
-    if (threadIdx.x == 0) inexact = 0;
-    __syncthreads();
-    for (uint32_t r = threadIdx.x; r < T.rows; r += blockDim.x) {
-      const float gr = __fmul_rn(T.scale, T.row_scales[r]);
-      if (!(__fmul_rn(__fmul_rn(gr, 0.5f), 2.0f) == gr)) inexact = 1;
+  if (blockIdx.x >= 16) {
+    // per-row multipliers, 1024 rows per block: (2 z + c) * (g / 2) equals
+    // (z + c/2) * g exactly whenever g / 2 is exact; the pair (g/2, g) is
+    // stored and a tensor with any row where g / 2 is inexact uses g.
+    const uint32_t r0 = (blockIdx.x - 16) * 1024u;
+    bool inexact = false;
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+      const uint32_t r = r0 + threadIdx.x + 256u * i;
+      if (r < T.rows) {
+        const float gr = __fmul_rn(T.scale, T.row_scales[r]);
+        const float h = __fmul_rn(gr, 0.5f);
+        inexact |= !(__fmul_rn(h, 2.0f) == gr);
+        reinterpret_cast<float2*>(T.rowv)[r] = make_float2(h, gr);
+      }
     }
-    __syncthreads();
-    const bool slow = inexact != 0;
-    for (uint32_t r = threadIdx.x; r < T.rows; r += blockDim.x) {
-      const float gr = __fmul_rn(T.scale, T.row_scales[r]);
-      T.rowv[r] = slow ? gr : __fmul_rn(gr, 0.5f);
-    }
-    if (threadIdx.x == 0) T.slow_rows = slow ? 1u : 0u;
+    if (inexact) atomicOr(&T.slow_rows, 1u);
     return;
   }
   const uint32_t k = 1 + blockIdx.x;            // table index 1..16
@@ -353,7 +353,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t vpr = T.vpr;
   const uint32_t out_bytes = T.out_bytes;
   const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, out_bytes);
-  const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 4u);
+  const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 8u);
 
   // ---- per-half-wave uniform state (scalar registers)
   const uint32_t n0 = __builtin_amdgcn_readlane(n, 0), n1 = __builtin_amdgcn_readlane(n, 32);
@@ -396,11 +396,12 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   __builtin_amdgcn_raw_buffer_store_b32(0u, rO, out_bytes, 0, 0);
 
   uint32_t g = t * T.V + l;                                 // < 2^32: checked on the host
-  uint32_t row4 = 0, col = 0;                               // row4: byte offset of the row multiplier
+  // rowb: byte offset of the row multiplier, g/2 or (slow rows) g of the row's pair
+  uint32_t rowb = slow_rows ? 4u : 0u, col = 0;
   if (tile_ok) {
     const uint32_t row = g / vpr;
     col = g - row * vpr;
-    row4 = 4u * row;
+    rowb += 8u * row;
   }
 
   // One vector round.  In full rounds every lane of both halves has a vector,
@@ -412,7 +413,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     const uint32_t x_saved = x;
     // Issued before the ring prefetch below: loads retire in order, so waiting
     // for this one later does not also wait for the prefetch.
-    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, row4, 0, 0));
+    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, rowb, 0, 0));
 
     // ---- ring: store the held chunk if it is useful and fits ...
     {
@@ -594,10 +595,10 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     col += 32u;
     if (col >= vpr) {                       // rows of at least 32 vectors wrap at most once
       col -= vpr;
-      row4 += 4u;
+      rowb += 8u;
       while (col >= vpr) {
         col -= vpr;
-        row4 += 4u;
+        rowb += 8u;
       }
     }
   };
@@ -783,7 +784,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     L.tab_off[i] = off;
     off = align256(off + (descs[i].num_tiles ? L.tab_bytes[i] : 0));
     L.row_off[i] = off;
-    off = align256(off + (descs[i].num_tiles ? 4 * size_t(descs[i].rows) : 0));
+    off = align256(off + (descs[i].num_tiles ? 8 * size_t(descs[i].rows) : 0));
   }
   L.total = std::max<size_t>(off, 256);
   return EP_OK;
@@ -1004,7 +1005,10 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   hipError_t e = hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
   if (n > 0) {
-    hipLaunchKernelGGL(build_tables_kernel, dim3(17, n), dim3(256), 0, st,
+    uint64_t max_rows = 1;
+    for (int i = 0; i < n; ++i) max_rows = std::max<uint64_t>(max_rows, uint64_t(descs[i].rows));
+    const uint32_t row_blocks = uint32_t((max_rows + 1023) / 1024);
+    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks, n), dim3(256), 0, st,
                        reinterpret_cast<DevTensor*>(wsb + L.tens_off));
     e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
