@@ -328,3 +328,26 @@ def test_hybrid_layout_large_alphabets(target, b, outliers):
     print(f"[hybrid] target={target} b={ct.b} A={amax}", flush=True)
     assert ct.b == b and amax > (1024 if b == 11 else 256)
     _check_parity(ct, kinds=("lattice2x", "bf16", "fp8", "uint8"), label=f"hybrid b={b} A={amax}")
+
+
+def test_rows_whose_half_multiplier_is_inexact():
+    # g = fp32(s * r) subnormal with an odd last bit: g/2 is not exact, so the tensor
+    # takes the (z + c/2) * g product; decoded in one batch beside an ordinary tensor
+    W = synthgen.student_t_weights(48, 512, 33).numpy()
+    ct = oracle.encode(W, 4.0, V=64)
+    rs = ct.row_scales.copy()
+    rs[3] = np.float32(3e-39)
+    rs[10] = np.float32(-7.3e-40)
+    g = (np.float32(ct.s) * rs[[3, 10]]).astype(np.float32)
+    half = (g * np.float32(0.5)).astype(np.float32)
+    assert np.any((half * np.float32(2.0)).astype(np.float32) != g)      # the slow case is hit
+    slow = dataclasses.replace(ct, row_scales=rs)
+    plain = oracle.encode(synthgen.student_t_weights(32, 256, 34).numpy(), 4.0, V=32)
+    for kind in ("fp32", "bf16", "fp16", "lattice2x"):
+        packed = [ep.PackedTensor.from_arrays(c) for c in (slow, plain)]
+        outs, sts = ep.decode_batch(packed, kind, with_status=True)
+        torch.cuda.synchronize()
+        for c, o, s_ in zip((slow, plain), outs, sts):
+            ref, _ = oracle.decode(c, kind)
+            assert np.all(s_.cpu().numpy()[: c.T] == 0)
+            assert np.array_equal(_gpu_out_numpy(o, kind), _ref_bits(ref, kind)), kind
