@@ -153,6 +153,33 @@ def build_inputs(specs, threads: int, device: str, cache_dir: str = "", host_enc
     return packed, hosts
 
 
+def weight_error(specs, outs, dtypes, route_scales, device: str) -> float:
+    """The model card's weight error in %: sqrt(sum ||W_hat - W||^2) / sqrt(sum ||W||^2).
+
+    W is each tensor's input, drawn again from its seed; W_hat is the decoded
+    output (FP8 / INT8 codes times the route's row scale, i.e. against the
+    original weights as in the paper's Table 7).  Sums in float64 on the device.
+    """
+    import torch
+
+    num = torch.zeros((), dtype=torch.float64, device=device)
+    den = torch.zeros((), dtype=torch.float64, device=device)
+    for spec, o, dt, q in zip(specs, outs, dtypes, route_scales):
+        W = spec.weights(device=device).double()
+        if dt == "fp8":
+            Wh = o.view(torch.float8_e4m3fn).float().double()
+        elif dt in ("int8", "uint8"):
+            Wh = o.double() - (128.0 if dt == "uint8" else 0.0)
+        else:
+            Wh = o.double()
+        if q is not None:
+            Wh = Wh * q[: W.shape[0], None].double()
+        num += ((Wh - W) ** 2).sum()
+        den += (W ** 2).sum()
+        del W, Wh
+    return float(100.0 * torch.sqrt(num / den)) if float(den) > 0 else 0.0
+
+
 def cpu_baseline(hosts, dtype: str, budget_s: float, threads: int):
     """The CPU oracle (untuned) decoding whole tensors of the workload on the host.
 
@@ -575,6 +602,15 @@ def main():
     ep.BatchArgs(packed, dtypes, outs, sts, ws).call(sp)
     torch.cuda.synchronize()
     tiles_ok = all(bool((s[: p.T] == 0).all()) for s, p in zip(sts, packed))
+    # reconstruction quality of what was timed (after the timed region)
+    import numpy as np
+    qs = []
+    for h in (hosts.results if isinstance(hosts, DeviceHosts) else hosts):
+        q = h.route_scales
+        if q is not None and not isinstance(q, torch.Tensor):
+            q = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).to(device)
+        qs.append(q)
+    rel_l2 = weight_error(specs, outs, dtypes, qs, device)
 
     algo_bytes = stored + out_bytes
     achieved = algo_bytes / (kms / 1e3) / 1e9
@@ -606,6 +642,7 @@ def main():
             "step_ms_min": min(step_ms),
             "hbm_roofline_frac_of_step": algo_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "tiles_ok": tiles_ok,
+            "weight_error_pct": rel_l2,
             "copy_gbs_measured": None,
         },
         "roofline": {
