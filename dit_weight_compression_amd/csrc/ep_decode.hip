@@ -32,7 +32,6 @@
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -362,6 +361,11 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t end0 = __builtin_amdgcn_readlane(pend, 0) - a00;
   const uint32_t end1 = __builtin_amdgcn_readlane(pend, 32) - a01;
   uint32_t P0 = st0 - a00, P1 = st1 - a01;                  // ring-relative read pointers
+  // the read pointer of this lane's half, kept per lane so that the
+  // renormalisation needs no scalar bookkeeping; P0 / P1 are refreshed from it
+  // once per round for the ring fill
+  uint32_t vP = half ? P1 : P0;
+  const uint32_t hs32 = half << 5;                          // selects this half's 32 ballot bits
   uint32_t F0 = 0, F1 = 0;                                  // words written to the ring
   uint64_t empty_err = 0;
   const uint32_t lane4 = 4u * l;                            // this lane's words inside a chunk
@@ -409,12 +413,13 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   auto round = [&](const uint32_t k, auto full) __attribute__((always_inline)) {
     constexpr bool kFull = decltype(full)::value;
     const bool active = kFull || (k * 32u + l) < n;
-    const uint64_t actm = kFull ? ~uint64_t(0) : __builtin_amdgcn_ballot_w64(active);
     const uint32_t x_saved = x;
     // Issued before the ring prefetch below: loads retire in order, so waiting
     // for this one later does not also wait for the prefetch.
     const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, rowb, 0, 0));
 
+    P0 = __builtin_amdgcn_readlane(vP, 0);
+    P1 = __builtin_amdgcn_readlane(vP, 32);
     // ---- ring: store the held chunk if it is useful and fits ...
     {
       const bool w0 = F0 < end0 && F0 <= P0 + kRingSlack;
@@ -447,21 +452,21 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16),
                                               0, 0);
 
+// Renormalisation: the lanes of a half whose state fell below 2^15 read the
+// next words of their tile in lane order.  A lane's word is its half's pointer
+// plus the number of reading lanes below it in the half (popcount of the
+// half's ballot bits under the lane).  Every lane reads (the index stays
+// inside the ring) and keeps the word only if it needed one: no exec masking
+// and no scalar pointer updates on the serial path.
 #define EP_RENORM()                                                                   \
   {                                                                                   \
-    const uint64_t nm = __builtin_amdgcn_ballot_w64(x < kL) & actm;                   \
-    const uint32_t nlo = uint32_t(nm), nhi = uint32_t(nm >> 32);                      \
-    const uint32_t clo = __builtin_popcount(nlo), chi = __builtin_popcount(nhi);      \
-    /* both halves' ring pointers in one scalar: half 1 pre-corrected for the      \
-       half-0 bits that mbcnt_lo also counts; only the low 9 bits matter */         \
-    const u16x2 pkv = {uint16_t(P0), uint16_t(P1 - clo)};                             \
-    const uint32_t pk = __builtin_bit_cast(uint32_t, pkv);                            \
-    if ((x < kL) & active) {                                                          \
-      const uint32_t idx = __builtin_amdgcn_mbcnt_hi(nhi, __builtin_amdgcn_mbcnt_lo(nlo, pk >> hs)); \
-      x = (x << 16) | ring[idx & (kRingWords - 1u)];                                  \
-    }                                                                                 \
-    P0 += clo;                                                                        \
-    P1 += chi;                                                                        \
+    const bool rn = (x < kL) & active;                                                \
+    const uint32_t hm = uint32_t(__builtin_amdgcn_ballot_w64(rn) >> hs32);            \
+    const uint32_t idx = __builtin_popcount(__builtin_amdgcn_ubfe(hm, 0, l)) + vP;    \
+    uint32_t w = ring[idx & (kRingWords - 1u)];                                       \
+    asm volatile("" : "+v"(w)); /* keep the read unconditional */                    \
+    x = rn ? ((x << 16) | w) : x;                                                     \
+    vP += __builtin_popcount(hm);                                                     \
   }
 
     // ---- field 0: coset bit (two-symbol table, resolved by one compare)
@@ -611,7 +616,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint64_t bad_state = __builtin_amdgcn_ballot_w64(x != kL);
   const uint64_t bad_len_m = __builtin_amdgcn_ballot_w64(bad_len);
   if (tile_ok && l == 0 && T.status) {
-    const uint32_t Pm = half ? P1 : P0, Em = half ? end1 : end0;
+    const uint32_t Pm = vP, Em = half ? end1 : end0;
     const uint32_t sh = half ? 32u : 0u;
     int st = EP_TILE_OK;
     if (uint32_t(bad_len_m >> sh)) st = EP_TILE_BAD_LENGTH;
