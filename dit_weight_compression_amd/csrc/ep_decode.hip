@@ -313,7 +313,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // probability precision when known at compile time (0: read T.b), TL the
 // table layout (LDS tables start at LDS address 0), OK the output kind.
 template <int BT, int TL, int OK>
-__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, uint32_t tiles_per_chunk,
+__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
                                             const unsigned char* __restrict__ lds,
                                             uint16_t* __restrict__ ring) {
   constexpr bool kWs = TL == kTabWorkspace;
@@ -327,9 +327,8 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t half = lane >> 5;
   const uint32_t hs = half << 4;                            // selects this half's packed 16 bits
   const uint32_t l = lane & 31u;
-  const uint32_t slot = 2u * (threadIdx.x >> 6) + half;   // tile of this half-wave within the chunk
-  const uint32_t t = tile0 + slot;
-  const bool tile_ok = slot < tiles_per_chunk && t < T.T;
+  const uint32_t t = tile0 + half;                          // tile of this half-wave
+  const bool tile_ok = t < tile_end;                        // tile_end <= T.T
 
   // ---- per-lane tile start
   uint32_t n = 0, x = kL, p = 0, pend = 0;
@@ -628,34 +627,54 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   }
 }
 
-// Persistent decode kernel: block i walks a contiguous range of chunks (up to 32
-// tiles of one tensor each; half-wave s of the block takes tile s of a chunk).
-// LDS layouts stage the tensor's decode tables once per run of chunks from the
-// same tensor.
+// Persistent decode kernel.  Block i owns a contiguous range of chunks (up to
+// tiles_per_chunk tiles of one tensor each), which splits into runs of chunks
+// from the same tensor.  For each run the block stages the tensor's decode
+// tables (LDS layouts); then each wave takes pairs of consecutive tiles (one
+// per half-wave) from a counter until the run is exhausted.  Taking work
+// dynamically keeps all of a block's waves busy to the end: the SIMD's issue
+// arbitration favours older waves, so equal static shares finish at very
+// different times.  The counter of a run is the word of `ctr` at the run's
+// first chunk (LDS is fully used by the tables and rings); a wave claims its
+// next pair before decoding the current one, so the atomic's latency is hidden.
 template <int BT, int TL, int OK>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
                                                         const Chunk* __restrict__ chunks,
+                                                        uint32_t* __restrict__ ctr,
                                                         uint32_t nchunks, uint32_t tiles_per_chunk) {
   constexpr size_t kTab = lds_table_bytes_of(TL, BT);
   __shared__ __align__(16) unsigned char smem[kTab + kRingBytes];
   const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
   const uint32_t c0 = blockIdx.x * per;
   const uint32_t c1 = min(nchunks, c0 + per);
+  const bool lane0 = (threadIdx.x & 63u) == 0;
   // LDS: [decode tables (LDS layouts)][32 rings of kRingWords]
   uint16_t* ring = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 5) * kRingWords;
-  uint32_t cur = 0xFFFFFFFFu;
-  for (uint32_t ci = c0; ci < c1; ++ci) {
+  for (uint32_t ci = c0; ci < c1;) {
     const Chunk ch = chunks[ci];
     const DevTensor& T = tens[ch.tensor];
-    if (TL != kTabWorkspace && ch.tensor != cur) {
-      __syncthreads();
+    // a tensor's chunks are consecutive: the run ends with the tensor or the range
+    const uint32_t left = (T.T - ch.tile0 + tiles_per_chunk - 1) / tiles_per_chunk;
+    const uint32_t cn = min(c1, ci + left);
+    const uint32_t t_end = min(T.T, ch.tile0 + (cn - ci) * tiles_per_chunk);
+    const uint32_t npairs = (t_end - ch.tile0 + 1) / 2;
+    __syncthreads();                       // every wave is done with the previous run
+    if (threadIdx.x == 0) __hip_atomic_store(ctr + ci, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (TL != kTabWorkspace) {
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)T.tab;
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
       for (uint32_t i = threadIdx.x; i < uint32_t(kTab / 16u); i += kBlock) dst[i] = src[i];
-      __syncthreads();
     }
-    cur = ch.tensor;
-    decode_pair<BT, TL, OK>(T, ch.tile0, tiles_per_chunk, smem, ring);
+    __syncthreads();
+    uint32_t nx = 0;
+    if (lane0) nx = atomicAdd(ctr + ci, 1u);
+    for (;;) {
+      const uint32_t pr = __builtin_amdgcn_readfirstlane(nx);
+      if (pr >= npairs) break;
+      if (lane0) nx = atomicAdd(ctr + ci, 1u);
+      decode_pair<BT, TL, OK>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+    }
+    ci = cn;
   }
 }
 
@@ -716,7 +735,7 @@ int out_kind_of(int dtype) {
 }
 
 struct Layout {
-  size_t tens_off, chunk_off, total;
+  size_t tens_off, chunk_off, ctr_off, total;
   std::vector<size_t> tab_off, tab_bytes, row_off;
   std::vector<uint32_t> variant, group;
   size_t max_chunks;                  // chunk slots for the smallest chunk (2 tiles)
@@ -785,6 +804,8 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   if (L.max_chunks >= (size_t(1) << 31)) return fail(EP_ERR_UNSUPPORTED, "too many tiles in one call");
   L.chunk_off = off;
   off = align256(off + sizeof(Chunk) * L.max_chunks);
+  L.ctr_off = off;                    // one work counter per chunk slot
+  off = align256(off + sizeof(uint32_t) * L.max_chunks);
   for (int i = 0; i < n; ++i) {
     L.tab_off[i] = off;
     off = align256(off + (descs[i].num_tiles ? L.tab_bytes[i] : 0));
@@ -803,12 +824,13 @@ struct PlanImpl {
   void* ws;
   uint64_t magic;
   uint64_t ntensors;
+  uint64_t ctr_off;                   // workspace offset of the per-chunk work counters
   Group groups[kNumGroups];
 };
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
-constexpr uint64_t kPlanMagic = 0x45504c414e763035ull;
+constexpr uint64_t kPlanMagic = 0x45504c414e763036ull;
 
-using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t, uint32_t);
+using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t*, uint32_t, uint32_t);
 
 template <int BT, int TL>
 KernelFn kernel_for_kind(int ok) {
@@ -1019,6 +1041,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
   }
   P->ws = workspace;
+  P->ctr_off = L.ctr_off;
   P->ntensors = uint64_t(n);
   P->magic = kPlanMagic;
   return EP_OK;
@@ -1035,7 +1058,8 @@ int ep_batch_launch(const ep_batch_plan* plan, void* stream) {
     const Group& G = P->groups[v];
     if (G.nchunks == 0) continue;
     hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), tens,
-                       chunks + G.chunk_begin, G.nchunks, G.tiles_per_chunk);
+                       chunks + G.chunk_begin, reinterpret_cast<uint32_t*>(wsb + P->ctr_off) + G.chunk_begin,
+                       G.nchunks, G.tiles_per_chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   }

@@ -127,9 +127,9 @@ int ep_abi_version(void);
 
 /*
  * Bytes of device workspace ep_decode_batch needs for these n tensors
- * (descriptors, per-tensor decode tables, the tile schedule).  Reads only
- * the host-side fields of the descriptors.  Returns EP_OK or
- * EP_ERR_INVALID_ARG; *bytes is set on success.
+ * (descriptors, per-tensor decode tables, the tile schedule and its work
+ * counters).  Reads only the host-side fields of the descriptors.  Returns
+ * EP_OK or EP_ERR_INVALID_ARG; *bytes is set on success.
  */
 int ep_workspace_size(const ep_tensor_desc* descs, int n, size_t* bytes);
 
@@ -141,6 +141,7 @@ int ep_workspace_size(const ep_tensor_desc* descs, int n, size_t* bytes);
  *   tile_status    NULL, or host array of n device pointers (each NULL or int32[num_tiles])
  *   workspace      device buffer of at least ep_workspace_size(descs, n) bytes,
  *                  256-byte aligned; reused and overwritten by every call
+ *                  (the decode kernel also updates work counters there)
  *   stream         hipStream_t
  * Calls that share a workspace must be ordered on one stream.
  */
