@@ -313,16 +313,20 @@ def _time_ms(fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def linear_overhead(tokens, threads: int, reps: int):
-    """Reconstruct-then-GEMM linear call against a resident BF16 weight.
+def linear_overhead(tokens, threads: int, reps: int, routes=("bf16", "fp8", "int8")):
+    """Reconstruct-then-GEMM linear call against a resident weight.
 
-    The paper's reference layer shape (10240 x 3840, 4 bpp): per call the
-    compressed weight is decoded into a BF16 scratch buffer (ep_batch_launch
-    with a prepared plan, and the complete ep_decode_batch call), then
-    y = x W^T runs as a library BF16 GEMM.  Reported per token count: the
-    resident GEMM time, both compressed-call times and the relative overhead.
-    The compressed path's output is checked bit for bit against the resident
-    GEMM on the same decoded weights.
+    The paper's reference layer shape (10240 x 3840, 4 bpp).  Per call the
+    compressed weight is decoded into a scratch buffer (ep_batch_launch with a
+    prepared plan; for BF16 also the complete ep_decode_batch call), then the
+    layer runs as a library GEMM: BF16 x BF16 for the direct container; for the
+    FP8 / INT8 routes (the paper's Table 7) the decoded codes feed an FP8
+    (torch._scaled_mm, per-token activation scale, per-row weight scale) or
+    INT8 (torch._int_mm, then the same two scales) GEMM on activations
+    quantised beforehand.  Reported per token count: the resident GEMM time,
+    the compressed-call times and the relative overhead.  The compressed
+    path's output is checked bit for bit against the resident GEMM on the same
+    decoded weights.
     """
     import torch
 
@@ -332,36 +336,68 @@ def linear_overhead(tokens, threads: int, reps: int):
 
     spec = synthgen.workload("ref_layer_10240x3840_4bpp_bf16")[0]
     W = spec.weights(device="cuda:0")
-    ct = encoder.encode(W.cpu().numpy(), spec.target_bpp, threads=threads)
-    p = ep.PackedTensor.from_arrays(ct, device="cuda:0", stored_bytes=ct.stored_bytes)
-    scratch = torch.empty((p.rows, p.cols), dtype=torch.bfloat16, device="cuda:0")
-    ws = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda:0")
-    batch = ep.BatchArgs([p], ["bf16"], [scratch], None, ws)
-    stream = torch.cuda.current_stream()
-    sp = ep.C.c_void_p(stream.cuda_stream)
-    plan = batch.prepare(sp)
-    batch.launch(plan, sp)
-    resident = scratch.clone()
     gen = torch.Generator(device="cuda:0")
-    gen.manual_seed(7)
-    rows = []
-    for T in tokens:
-        x = torch.randn(T, p.cols, generator=gen, device="cuda:0").to(torch.bfloat16)
-        y_res = torch.matmul(x, resident.t())
+    out = []
+    for route in routes:
+        if route == "bf16":
+            ct = encoder.encode(W.cpu().numpy(), spec.target_bpp, threads=threads)
+            p = ep.PackedTensor.from_arrays(ct, device="cuda:0", stored_bytes=ct.stored_bytes)
+            q = None
+            stored = ct.stored_bytes
+        else:
+            d = ep.encode_device(W, spec.target_bpp, route=route)
+            p, q = d.packed, d.route_scales.float()
+            stored = p.stored_bytes
+        scratch = torch.empty((p.rows, p.cols), dtype=torch.bfloat16 if route == "bf16" else torch.uint8,
+                              device="cuda:0")
+        ws = torch.empty(ep.workspace_size([p]), dtype=torch.uint8, device="cuda:0")
+        batch = ep.BatchArgs([p], [route], [scratch], None, ws)
+        sp = ep.C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        plan = batch.prepare(sp)
         batch.launch(plan, sp)
-        y_cmp = torch.matmul(x, scratch.t())
-        torch.cuda.synchronize()
-        exact = bool(torch.equal(y_res, y_cmp))
-        t_res = _time_ms(lambda: torch.matmul(x, resident.t()), reps)
-        t_launch = _time_ms(lambda: (batch.launch(plan, sp), torch.matmul(x, scratch.t())), reps)
-        t_full = _time_ms(lambda: (batch.call(sp), torch.matmul(x, scratch.t())), reps)
-        t_dec = _time_ms(lambda: batch.launch(plan, sp), reps)
-        rows.append({"tokens": T, "gemm_ms": t_res, "decode_launch_ms": t_dec,
-                     "compressed_call_ms": t_launch, "compressed_full_call_ms": t_full,
-                     "overhead": t_launch / t_res - 1.0, "overhead_full_call": t_full / t_res - 1.0,
-                     "output_bit_exact": exact})
-    print(json.dumps({"linear_call": {"layer": [p.rows, p.cols], "stored_bpp": 8.0 * ct.stored_bytes / p.numel,
-                                      "gemm": "torch.matmul bf16", "points": rows}}), flush=True)
+        resident = scratch.clone()
+        gen.manual_seed(7)
+        form = "torch.matmul bf16"
+        rows = []
+        for T in tokens:
+            x = torch.randn(T, p.cols, generator=gen, device="cuda:0").to(torch.bfloat16)
+            if route == "bf16":
+                def gemm(w, x=x):
+                    return torch.matmul(x, w.t())
+            elif route == "fp8":
+                sx = (x.float().abs().amax(dim=1, keepdim=True) / 448.0).clamp_min(1e-12)
+                x8 = (x.float() / sx).to(torch.float8_e4m3fn)
+                sw = q[None, :].contiguous()
+
+                def gemm(w, x8=x8, sx=sx, sw=sw):
+                    return torch._scaled_mm(x8, w.view(torch.float8_e4m3fn).t(), scale_a=sx, scale_b=sw,
+                                            out_dtype=torch.bfloat16)
+                form = "torch._scaled_mm fp8 e4m3fn, row-wise scales"
+            else:
+                sx = (x.float().abs().amax(dim=1, keepdim=True) / 127.0).clamp_min(1e-12)
+                x8 = torch.round(x.float() / sx).clamp_(-127, 127).to(torch.int8)
+                sxw = sx * q[None, :]
+
+                def gemm(w, x8=x8, sxw=sxw):
+                    return (torch._int_mm(x8, w.view(torch.int8).t()).float() * sxw).to(torch.bfloat16)
+                form = "torch._int_mm int8, then the row / token scales"
+            y_res = gemm(resident)
+            batch.launch(plan, sp)
+            y_cmp = gemm(scratch)
+            torch.cuda.synchronize()
+            exact = bool(torch.equal(y_res, y_cmp))
+            t_res = _time_ms(lambda: gemm(resident), reps)
+            t_launch = _time_ms(lambda: (batch.launch(plan, sp), gemm(scratch)), reps)
+            t_full = _time_ms(lambda: (batch.call(sp), gemm(scratch)), reps)
+            t_dec = _time_ms(lambda: batch.launch(plan, sp), reps)
+            rows.append({"tokens": T, "gemm_ms": t_res, "decode_launch_ms": t_dec,
+                         "compressed_call_ms": t_launch, "compressed_full_call_ms": t_full,
+                         "overhead": t_launch / t_res - 1.0, "overhead_full_call": t_full / t_res - 1.0,
+                         "output_bit_exact": exact})
+            log(json.dumps({"route": route, **rows[-1]}))
+        out.append({"route": route, "stored_bpp": 8.0 * stored / p.numel, "gemm": form, "points": rows})
+        del scratch, resident, ws, batch
+    print(json.dumps({"linear_call": {"layer": [spec.rows, spec.cols], "routes": out}}), flush=True)
 
 
 def tile_sweep(sizes, threads: int, reps: int):

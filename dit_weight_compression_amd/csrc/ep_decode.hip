@@ -666,13 +666,13 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       for (uint32_t i = threadIdx.x; i < uint32_t(kTab / 16u); i += kBlock) dst[i] = src[i];
     }
     __syncthreads();
-    uint32_t nx = 0;
-    if (lane0) nx = atomicAdd(ctr + ci, 1u);
-    for (;;) {
-      const uint32_t pr = __builtin_amdgcn_readfirstlane(nx);
-      if (pr >= npairs) break;
-      if (lane0) nx = atomicAdd(ctr + ci, 1u);
+    // the first pair of each wave is its own index, which spreads a short run
+    // over the SIMDs (wave w runs on SIMD w mod 4); later pairs come from the counter
+    uint32_t pr = threadIdx.x >> 6, nx = 0;
+    while (pr < npairs) {
+      if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
       decode_pair<BT, TL, OK>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+      pr = __builtin_amdgcn_readfirstlane(nx);
     }
     ci = cn;
   }
