@@ -119,6 +119,12 @@ def _declare(L):
     L.epo_bpp.restype = f64
     L.epo_rel_l2.argtypes = [vp, vp, i64]
     L.epo_rel_l2.restype = f64
+    L.epo_rdo_ratios.argtypes = [u32, vp]
+    L.epo_encode_rdo.argtypes = [vp, i64, i64, f64, u32, u32, C.c_int, u32, u32, _p(vp)]
+    L.epo_encode_rdo.restype = C.c_int
+    L.epo_rdo_trace.argtypes = [vp, i64, i64, f64, u32, u32, C.c_int, u32, vp, vp, vp, _p(i64),
+                                _p(f64), vp, _p(f32), _p(u32)]
+    L.epo_rdo_trace.restype = C.c_int
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -352,6 +358,48 @@ def encode_fixed_scale(W, s: float, V: int, b: int, route: str = "direct") -> Co
         return _from_handle(h)
     finally:
         lib().epo_tensor_free(h)
+
+
+def rdo_ratios(K: int) -> np.ndarray:
+    """The K nested candidate ratios of the per-row refinement (rho_1 = 1 first)."""
+    out = np.zeros(max(K, 1), np.float64)
+    lib().epo_rdo_ratios(K, _ptr(out))
+    return out[:K]
+
+
+def encode_rdo(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct", K: int = 5,
+               sweeps: int = 1) -> Container:
+    """encode() followed by the per-row rate-distortion refinement (K candidate
+    resolutions per row, `sweeps` model-update and selection sweeps)."""
+    W = _c(W, np.float32)
+    R, Cc = W.shape
+    h = C.c_void_p()
+    rc = lib().epo_encode_rdo(_ptr(W), R, Cc, float(target_bpp), V, b, ROUTES[route], K, sweeps, C.byref(h))
+    if rc != 0:
+        raise ValueError(f"oracle encode_rdo failed: {rc}")
+    try:
+        return _from_handle(h)
+    finally:
+        lib().epo_tensor_free(h)
+
+
+def rdo_trace(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct", K: int = 5) -> dict:
+    """The refinement's first sweep: distortions D [rows, K], rates R [rows, K]
+    (units of 2^-16 bit), candidate row scales, the budget, lambda and the
+    selection; s and b of the baseline."""
+    W = _c(W, np.float32)
+    R, Cc = W.shape
+    D = np.zeros((R, K), np.float64)
+    Rt = np.zeros((R, K), np.int64)
+    rs = np.zeros((R, K), np.float32)
+    sel = np.zeros(R, np.int32)
+    budget, lam, s, bb = C.c_int64(), C.c_double(), C.c_float(), C.c_uint32()
+    rc = lib().epo_rdo_trace(_ptr(W), R, Cc, float(target_bpp), V, b, ROUTES[route], K, _ptr(D), _ptr(Rt),
+                             _ptr(rs), C.byref(budget), C.byref(lam), _ptr(sel), C.byref(s), C.byref(bb))
+    if rc != 0:
+        raise ValueError(f"oracle rdo_trace failed: {rc}")
+    return {"D": D, "R": Rt, "row_scales": rs, "budget": budget.value, "lambda": lam.value, "sel": sel,
+            "s": s.value, "b": bb.value}
 
 
 def decode(ct: Container, kind: str = "bf16", tile_begin: int = 0, tile_end: Optional[int] = None,

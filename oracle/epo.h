@@ -16,7 +16,9 @@
  * Pins (tests/test_oracle_*.py, tests/golden/): brute force and the E8
  * constants for the lattice, round trips and code-length bounds for rANS,
  * Table 5's tile accounting and Table 4's rate effects, closed forms for the
- * row statistics and the refit, library casts for every container rounding.
+ * row statistics and the refit, library casts for every container rounding,
+ * closed-form candidate ratios, recomputed distortions and brute-force
+ * Lagrangian optimality for the per-row refinement.
  * Parity unpinned against the pages (they print no stream bytes, scales,
  * samples or estimates): the E8 tie-breaks, the frequency normalisation rule,
  * the scale search's row sample and rate estimator, and the byte layout; each
@@ -113,6 +115,19 @@ int    epo_tensor_coding(const epo_tensor* t);
 /* Stored bytes of a coded container: pooled tables store 8 coordinate tables. */
 uint64_t epo_stored_bytes_coded(int64_t rows, uint32_t T, uint64_t nwords,
                                 const uint32_t alphabet[EPO_TABLES], int route, int coding);
+/* Per-row rate-distortion refinement (section 3.5, appendix C.2): K nested
+ * candidate ratios, `sweeps` model-update / selection sweeps, then the same
+ * container as epo_encode (standard coding) from the selected fields. */
+void   epo_rdo_ratios(uint32_t K, double* rho);
+int    epo_encode_rdo(const float* W, int64_t rows, int64_t cols, double target_bpp,
+                      uint32_t V, uint32_t b0, int route, uint32_t K, uint32_t sweeps,
+                      epo_tensor** out);
+/* The first sweep's quantities: D, R [rows*K] (R in 2^-16 bit), candidate row
+ * scales [rows*K], the budget, lambda and the selection [rows]; s and b of
+ * the baseline. */
+int    epo_rdo_trace(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
+                     uint32_t b0, int route, uint32_t K, double* D, int64_t* R, float* row_scales,
+                     int64_t* budget, double* lambda, int32_t* sel, float* s_out, uint32_t* b_out);
 void   epo_tensor_free(epo_tensor* t);
 void   epo_tensor_info(const epo_tensor* t, int64_t* rows, int64_t* cols, uint32_t* V,
                        uint32_t* T, uint32_t* b, float* s, uint64_t* nwords,

@@ -430,6 +430,41 @@ static float* prepare_input(const float* W, int64_t rows, int64_t cols, int rout
   return Wq;
 }
 
+/* Algorithm 1 with the precision escalation and coarsening of appendix C.1:
+ * returns the final scale, raises *b as needed, leaves the full tensor's
+ * fields at that scale in `fields` and the sampled rate estimate in *est. */
+static float baseline_scale(const float* Wq, int64_t rows, int64_t cols, const double* norms,
+                            double target_bpp, uint32_t V, int route, uint32_t* bp,
+                            int32_t* fields, double* est) {
+  int64_t* sample = (int64_t*)malloc(sizeof(int64_t) * (rows ? rows : 1));
+  int64_t nsample = 0;
+  epo_sample_rows(rows, cols, sample, &nsample);
+  int64_t nvec = rows * (cols / 8);
+  uint32_t b = *bp;
+  float s = 1.0f;
+  for (;;) {
+    double sd = scale_search(Wq, rows, cols, norms, sample, nsample, target_bpp, b, V, route);
+    *est = epo_estimate_bpp(Wq, rows, cols, norms, sample, nsample, sd, b, V, route);
+    s = (float)sd;
+    quantize_rows(Wq, cols, norms, NULL, rows, (double)s, fields);
+    uint32_t amax = max_coord_alphabet(fields, nvec);
+    if (amax <= (1u << b)) break;
+    if (b < 15) {
+      b += 1;
+      continue;
+    }
+    while (amax > (1u << b)) {
+      s = (float)(1.05 * (double)s * (double)amax / (double)(1u << b));
+      quantize_rows(Wq, cols, norms, NULL, rows, (double)s, fields);
+      amax = max_coord_alphabet(fields, nvec);
+    }
+    break;
+  }
+  free(sample);
+  *bp = b;
+  return s;
+}
+
 int epo_encode(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
                uint32_t b0, int route, epo_tensor** out) {
   return epo_encode_coded(W, rows, cols, target_bpp, V, b0, route, EPO_CODING_STANDARD, out);
@@ -450,35 +485,11 @@ int epo_encode_coded(const float* W, int64_t rows, int64_t cols, double target_b
   float* Wq = prepare_input(W, rows, cols, route, t);
   double* norms = (double*)malloc(sizeof(double) * (rows ? rows : 1));
   epo_row_rms(Wq, rows, cols, norms);
-  int64_t* sample = (int64_t*)malloc(sizeof(int64_t) * (rows ? rows : 1));
-  int64_t nsample = 0;
-  epo_sample_rows(rows, cols, sample, &nsample);
-
-  int64_t per_row = cols / 8;
-  int64_t nvec = rows * per_row;
+  int64_t nvec = rows * (cols / 8);
   int32_t* fields = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)(nvec ? nvec : 1));
-  float s = 1.0f;
-  for (;;) {
-    double sd = scale_search(Wq, rows, cols, norms, sample, nsample, target_bpp, b, V, route);
-    t->est_bpp = epo_estimate_bpp(Wq, rows, cols, norms, sample, nsample, sd, b, V, route);
-    s = (float)sd;
-    quantize_rows(Wq, cols, norms, NULL, rows, (double)s, fields);
-    uint32_t amax = max_coord_alphabet(fields, nvec);
-    if (amax <= (1u << b)) break;
-    if (b < 15) {
-      b += 1;
-      continue;
-    }
-    while (amax > (1u << b)) {
-      s = (float)(1.05 * (double)s * (double)amax / (double)(1u << b));
-      quantize_rows(Wq, cols, norms, NULL, rows, (double)s, fields);
-      amax = max_coord_alphabet(fields, nvec);
-    }
-    break;
-  }
+  float s = baseline_scale(Wq, rows, cols, norms, target_bpp, V, route, &b, fields, &t->est_bpp);
   int rc = finish_encode(Wq, rows, cols, s, b, V, fields, coding, t);
   free(fields);
-  free(sample);
   free(norms);
   free(Wq);
   if (rc != 0) {
@@ -642,5 +653,312 @@ int epo_decode_coded(int64_t rows, int64_t cols, uint32_t V, uint32_t T, uint32_
   }
   free(sym);
   epo__tables_free(tb);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Per-row rate-distortion refinement (paper, section 3.5 "Per-row
+ * rate-distortion refinement", appendix C.2 and appendix A.4).
+ *
+ * What the pages fix: each row chooses one of K quantisation resolutions
+ * rho_k * s with rho_1 = 1 and ratios inside [0.70, 1.45], added by bisecting
+ * the widest remaining interval in log scale, so the sets are nested; the
+ * candidates' fields, fitted row scales and distortions are computed once;
+ * each sweep updates the shared probability model from the selected fields
+ * and then selects the rows' candidates through one common rate penalty; the
+ * allocation keeps the single-scale baseline's storage.  Algorithm 2 itself
+ * is not printed.  Readings (listed in the design notes):
+ *  - The first interval bisected is the wider of [0.70, 1] and [1, 1.45] in
+ *    log scale (ties: the lower one); the bounds are not candidates.
+ *  - Distortion D_rk = sum over the row of (w - y)^2 in fp64, y being the
+ *    decoded fp32 value fp32(x * fp32(s * r_rk)) with the candidate's
+ *    least-squares row scale r_rk.
+ *  - Rate R_rk = sum over the row's symbols of (b_m - log2 f) bits under the
+ *    model's normalised tables (precision b_m = the smallest b' >= b that
+ *    holds the model's alphabets), a symbol the model does not hold costing
+ *    b_m bits; costs are kept in units of 2^-16 bit (rounded to nearest) so
+ *    that totals are exact integers.
+ *  - The budget is the baseline selection's total rate under the first
+ *    sweep's model.  The penalty lambda is the smallest one (to a 60-step
+ *    bisection) at which the rows' choices argmin_k D_rk + lambda R_rk (ties
+ *    to the lower k) fit the budget; lambda = 0 if the least-distortion
+ *    choices already fit.
+ *  - Sweeps stop early if the selected fields need more than 15 bits of
+ *    precision; the container keeps b if the final fields fit 2^b, raises it
+ *    otherwise (at most 15), and falls back to the baseline fields if even
+ *    that does not hold them.
+ * ------------------------------------------------------------------------ */
+
+void epo_rdo_ratios(uint32_t K, double* rho) {
+  /* log-scale intervals, kept sorted by position */
+  double lo[64], hi[64];
+  int n = 2;
+  lo[0] = log(0.70);
+  hi[0] = 0.0;
+  lo[1] = 0.0;
+  hi[1] = log(1.45);
+  if (K == 0) return;
+  rho[0] = 1.0;
+  for (uint32_t k = 1; k < K && n < 63; ++k) {
+    int w = 0;
+    for (int i = 1; i < n; ++i)
+      if (hi[i] - lo[i] > hi[w] - lo[w]) w = i;
+    double mid = 0.5 * (lo[w] + hi[w]);
+    rho[k] = exp(mid);
+    for (int i = n; i > w + 1; --i) lo[i] = lo[i - 1], hi[i] = hi[i - 1];
+    lo[w + 1] = mid;
+    hi[w + 1] = hi[w];
+    hi[w] = mid;
+    ++n;
+  }
+}
+
+/* model cost tables: cost[base[k] + i] in 2^-16 bit for value minv[k] + i */
+typedef struct {
+  int32_t minv[EPO_TABLES];
+  uint32_t A[EPO_TABLES];
+  uint32_t base[EPO_TABLES];
+  int64_t* cost;
+  int64_t miss;          /* cost of a symbol the model does not hold */
+} rdo_model;
+
+static int rdo_model_build(const int32_t* fields, int64_t nvec, uint32_t b, rdo_model* m) {
+  int32_t maxv[EPO_TABLES];
+  int has[EPO_TABLES];
+  table_ranges(fields, nvec, m->minv, maxv, has);
+  alphabets_from_ranges(m->minv, maxv, has, m->A);
+  uint32_t bm = b;
+  for (int k = 1; k < EPO_TABLES; ++k)
+    while (m->A[k] > (1u << bm) && bm < 15) ++bm;
+  for (int k = 1; k < EPO_TABLES; ++k)
+    if (m->A[k] > (1u << bm)) return -1;
+  uint32_t tot = 0;
+  for (int k = 0; k < EPO_TABLES; ++k) {
+    m->base[k] = tot;
+    tot += m->A[k];
+  }
+  m->cost = (int64_t*)malloc(sizeof(int64_t) * (tot ? tot : 1));
+  m->miss = (int64_t)65536 * (int64_t)bm;
+  uint64_t** counts = table_counts(fields, nvec, m->minv, m->A);
+  int rc = 0;
+  for (int k = 0; k < EPO_TABLES && rc == 0; ++k) {
+    if (m->A[k] == 0) continue;
+    uint16_t* f = (uint16_t*)malloc(sizeof(uint16_t) * m->A[k]);
+    if (epo_normalize_freqs(counts[k], m->A[k], bm, f) != 0) {
+      rc = -1;
+    } else {
+      for (uint32_t i = 0; i < m->A[k]; ++i)
+        m->cost[m->base[k] + i] =
+            f[i] ? llround(65536.0 * ((double)bm - log2((double)f[i]))) : m->miss;
+    }
+    free(f);
+  }
+  free_counts(counts);
+  if (rc != 0) free(m->cost);
+  return rc;
+}
+
+static int64_t rdo_row_rate(const int32_t* fl, int64_t per_row, const rdo_model* m) {
+  int64_t r = 0;
+  for (int64_t j = 0; j < per_row; ++j, fl += 9) {
+    int c = fl[0];
+    for (int f = 0; f < EPO_FIELDS; ++f) {
+      int k = epo_table_index(f, c);
+      int64_t i = (int64_t)fl[f] - (int64_t)m->minv[k];
+      r += (i >= 0 && i < (int64_t)m->A[k]) ? m->cost[m->base[k] + i] : m->miss;
+    }
+  }
+  return r;
+}
+
+/* rows' choices at penalty lam; returns their total rate */
+static int64_t rdo_choose(const double* D, const int64_t* R, int64_t rows, uint32_t K, double lam,
+                          int32_t* sel) {
+  int64_t tot = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    uint32_t best = 0;
+    double jb = D[r * K] + lam * ((double)R[r * K] / 65536.0);
+    for (uint32_t k = 1; k < K; ++k) {
+      double j = D[r * K + k] + lam * ((double)R[r * K + k] / 65536.0);
+      if (j < jb) jb = j, best = k;
+    }
+    if (sel) sel[r] = (int32_t)best;
+    tot += R[r * K + best];
+  }
+  return tot;
+}
+
+static double rdo_lambda(const double* D, const int64_t* R, int64_t rows, uint32_t K, int64_t budget) {
+  if (rdo_choose(D, R, rows, K, 0.0, NULL) <= budget) return 0.0;
+  double sd = 0.0, sr = 0.0;
+  for (int64_t r = 0; r < rows; ++r) sd += D[r * K], sr += (double)R[r * K] / 65536.0;
+  double hi = (sd > 0.0 && sr > 0.0) ? sd / sr : 1e-30;
+  double lo = 0.0;
+  int it = 0;
+  while (rdo_choose(D, R, rows, K, hi, NULL) > budget && it < 200) {
+    lo = hi;
+    hi *= 2.0;
+    ++it;
+  }
+  for (int i = 0; i < 60; ++i) {
+    double mid = 0.5 * (lo + hi);
+    if (rdo_choose(D, R, rows, K, mid, NULL) > budget) lo = mid;
+    else hi = mid;
+  }
+  return hi;
+}
+
+/* Candidates' fields [K][nvec * 9], row scales [rows * K] and distortions. */
+static void rdo_candidates(const float* Wq, int64_t rows, int64_t cols, const double* norms, float s,
+                           uint32_t K, const double* rho, int32_t* cand, float* rsc, double* D) {
+  int64_t per_row = cols / 8;
+  int64_t nvec = rows * per_row;
+  for (uint32_t k = 0; k < K; ++k) {
+    int32_t* fk = cand + (size_t)k * 9 * (size_t)nvec;
+    quantize_rows(Wq, cols, norms, NULL, rows, (double)s * rho[k], fk);
+    for (int64_t r = 0; r < rows; ++r) {
+      double num = 0.0, den = 0.0, x[8];
+      for (int64_t j = 0; j < per_row; ++j) {
+        epo_fields_to_point(fk + 9 * (r * per_row + j), x);
+        for (int q = 0; q < 8; ++q) {
+          double sx = (double)s * x[q];
+          num += (double)Wq[r * cols + 8 * j + q] * sx;
+          den += sx * sx;
+        }
+      }
+      float rs = den > 0.0 ? (float)(num / den) : 0.0f;
+      float gs = s * rs;
+      double d = 0.0;
+      for (int64_t j = 0; j < per_row; ++j) {
+        epo_fields_to_point(fk + 9 * (r * per_row + j), x);
+        for (int q = 0; q < 8; ++q) {
+          float y = (float)x[q] * gs;
+          double e = (double)Wq[r * cols + 8 * j + q] - (double)y;
+          d += e * e;
+        }
+      }
+      rsc[r * K + k] = rs;
+      D[r * K + k] = d;
+    }
+  }
+}
+
+static void rdo_gather(const int32_t* cand, int64_t rows, int64_t per_row, const int32_t* sel,
+                       int32_t* out) {
+  int64_t nvec = rows * per_row;
+  for (int64_t r = 0; r < rows; ++r)
+    memcpy(out + 9 * r * per_row, cand + (size_t)sel[r] * 9 * (size_t)nvec + 9 * r * per_row,
+           sizeof(int32_t) * 9 * (size_t)per_row);
+}
+
+/* The refinement proper.  trace (optional, first sweep only): D, R [rows*K],
+ * row scales [rows*K], budget, lambda, selection [rows]. */
+static int rdo_run(const float* Wq, int64_t rows, int64_t cols, const double* norms, float s,
+                   uint32_t b, uint32_t K, uint32_t sweeps, int32_t* fields, double* tD,
+                   int64_t* tR, float* tS, int64_t* tbudget, double* tlam, int32_t* tsel) {
+  int64_t per_row = cols / 8;
+  int64_t nvec = rows * per_row;
+  double rho[64];
+  epo_rdo_ratios(K, rho);
+  int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)K * (size_t)(nvec ? nvec : 1));
+  float* rsc = (float*)malloc(sizeof(float) * (size_t)K * (size_t)(rows ? rows : 1));
+  double* D = (double*)malloc(sizeof(double) * (size_t)K * (size_t)(rows ? rows : 1));
+  int64_t* R = (int64_t*)malloc(sizeof(int64_t) * (size_t)K * (size_t)(rows ? rows : 1));
+  int32_t* sel = (int32_t*)calloc((size_t)(rows ? rows : 1), sizeof(int32_t));
+  rdo_candidates(Wq, rows, cols, norms, s, K, rho, cand, rsc, D);
+  int64_t budget = -1;
+  for (uint32_t sw = 0; sw < sweeps; ++sw) {
+    rdo_gather(cand, rows, per_row, sel, fields);
+    rdo_model m;
+    if (rdo_model_build(fields, nvec, b, &m) != 0) break;
+    for (int64_t r = 0; r < rows; ++r)
+      for (uint32_t k = 0; k < K; ++k)
+        R[r * K + k] = rdo_row_rate(cand + (size_t)k * 9 * (size_t)nvec + 9 * r * per_row, per_row, &m);
+    free(m.cost);
+    if (budget < 0) {
+      budget = 0;
+      for (int64_t r = 0; r < rows; ++r) budget += R[r * K + sel[r]];
+    }
+    double lam = rdo_lambda(D, R, rows, K, budget);
+    rdo_choose(D, R, rows, K, lam, sel);
+    if (sw == 0) {
+      if (tD) memcpy(tD, D, sizeof(double) * (size_t)K * (size_t)rows);
+      if (tR) memcpy(tR, R, sizeof(int64_t) * (size_t)K * (size_t)rows);
+      if (tS) memcpy(tS, rsc, sizeof(float) * (size_t)K * (size_t)rows);
+      if (tbudget) *tbudget = budget;
+      if (tlam) *tlam = lam;
+      if (tsel) memcpy(tsel, sel, sizeof(int32_t) * (size_t)rows);
+    }
+  }
+  rdo_gather(cand, rows, per_row, sel, fields);
+  free(sel);
+  free(R);
+  free(D);
+  free(rsc);
+  free(cand);
+  return 0;
+}
+
+int epo_encode_rdo(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
+                   uint32_t b0, int route, uint32_t K, uint32_t sweeps, epo_tensor** out) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return -1;
+  if (route < 0 || route > 2 || K < 1 || K > 32) return -1;
+  if (V == 0) V = epo_default_vectors_per_tile(target_bpp);
+  if (V < 32) return -1;
+  uint32_t b = b0 ? b0 : epo_default_prob_bits(target_bpp);
+  if (b < 9 || b > 15) return -1;
+  if ((uint64_t)rows * (uint64_t)cols / 8u > 0xFFFFFFFFull) return -1;
+  epo_tensor* t = tensor_new(rows, cols, route);
+  float* Wq = prepare_input(W, rows, cols, route, t);
+  double* norms = (double*)malloc(sizeof(double) * (rows ? rows : 1));
+  epo_row_rms(Wq, rows, cols, norms);
+  int64_t nvec = rows * (cols / 8);
+  int32_t* base = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)(nvec ? nvec : 1));
+  float s = baseline_scale(Wq, rows, cols, norms, target_bpp, V, route, &b, base, &t->est_bpp);
+  int32_t* fields = base;
+  int32_t* sel = NULL;
+  if (K > 1 && sweeps > 0 && nvec > 0) {
+    sel = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)nvec);
+    rdo_run(Wq, rows, cols, norms, s, b, K, sweeps, sel, NULL, NULL, NULL, NULL, NULL, NULL);
+    uint32_t amax = max_coord_alphabet(sel, nvec), bf = b;
+    while (amax > (1u << bf) && bf < 15) ++bf;
+    if (amax <= (1u << bf)) {
+      fields = sel;
+      b = bf;
+    }
+  }
+  int rc = finish_encode(Wq, rows, cols, s, b, V, fields, EPO_CODING_STANDARD, t);
+  free(sel);
+  free(base);
+  free(norms);
+  free(Wq);
+  if (rc != 0) {
+    epo_tensor_free(t);
+    return rc;
+  }
+  *out = t;
+  return 0;
+}
+
+int epo_rdo_trace(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t V,
+                  uint32_t b0, int route, uint32_t K, double* D, int64_t* R, float* row_scales,
+                  int64_t* budget, double* lambda, int32_t* sel, float* s_out, uint32_t* b_out) {
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || K < 1 || K > 32) return -1;
+  if (V == 0) V = epo_default_vectors_per_tile(target_bpp);
+  uint32_t b = b0 ? b0 : epo_default_prob_bits(target_bpp);
+  epo_tensor* t = tensor_new(rows, cols, route);
+  float* Wq = prepare_input(W, rows, cols, route, t);
+  double* norms = (double*)malloc(sizeof(double) * (size_t)rows);
+  epo_row_rms(Wq, rows, cols, norms);
+  int64_t nvec = rows * (cols / 8);
+  int32_t* fields = (int32_t*)malloc(sizeof(int32_t) * 9 * (size_t)nvec);
+  float s = baseline_scale(Wq, rows, cols, norms, target_bpp, V, route, &b, fields, &t->est_bpp);
+  rdo_run(Wq, rows, cols, norms, s, b, K, 1, fields, D, R, row_scales, budget, lambda, sel);
+  *s_out = s;
+  *b_out = b;
+  free(fields);
+  free(norms);
+  free(Wq);
+  epo_tensor_free(t);
   return 0;
 }

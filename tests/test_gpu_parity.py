@@ -351,3 +351,24 @@ def test_rows_whose_half_multiplier_is_inexact():
             ref, _ = oracle.decode(c, kind)
             assert np.all(s_.cpu().numpy()[: c.T] == 0)
             assert np.array_equal(_gpu_out_numpy(o, kind), _ref_bits(ref, kind)), kind
+
+
+def test_large_batch_runs_and_work_counter():
+    """Enough small tiles to fill every resident block with full chunks.
+
+    12 tensors of 807 tiles (V = 32; the last chunk of each tensor partial)
+    make blocks whose chunk ranges straddle tensor boundaries, so blocks
+    decode several runs and take tile pairs beyond their first from the work
+    counter.  Every output is compared whole against the oracle.
+    """
+    cts = [oracle.encode(synthgen.student_t_weights(200, 1032, 700 + i).numpy(), 4.0, V=32) for i in range(12)]
+    assert all(ct.b == 11 and ct.T == 807 for ct in cts)
+    kinds = ["bf16"] * 12
+    packed = [ep.PackedTensor.from_arrays(c) for c in cts]
+    for rep in range(2):
+        outs, sts = ep.decode_batch(packed, kinds, with_status=True)
+        torch.cuda.synchronize()
+        for i, ct in enumerate(cts):
+            ref, _ = oracle.decode(ct, "bf16")
+            assert np.array_equal(_gpu_out_numpy(outs[i], "bf16"), ref), f"rep {rep} tensor {i}"
+            assert np.all(sts[i].cpu().numpy()[: ct.T] == 0)
