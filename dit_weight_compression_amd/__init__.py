@@ -28,7 +28,8 @@ EXPORTS = ["ep_status_string", "ep_last_error", "ep_abi_version", "ep_workspace_
            "ep_convert_f32"]
 # every symbol include/entropack_device_encode.h declares (same library)
 DEVICE_ENCODE_EXPORTS = ["ep_encode_device_workspace_size", "ep_encode_device",
-                         "ep_encode_device_emit"]
+                         "ep_encode_device_emit", "ep_encode_device_rdo_workspace_size",
+                         "ep_encode_device_rdo"]
 ROUTES = {"direct": 0, "fp8": 1, "int8": 2}
 CODINGS = {"standard": 0, "pooled": 1, "direct_z8": 2}   # ep_coding
 
@@ -101,6 +102,12 @@ def lib():
         L.ep_encode_device.restype = C.c_int
         L.ep_encode_device_emit.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_encode_device_emit.restype = C.c_int
+        L.ep_encode_device_rdo_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_uint32,
+                                                          C.c_int, C.c_uint32, C.POINTER(C.c_size_t)]
+        L.ep_encode_device_rdo_workspace_size.restype = C.c_int
+        L.ep_encode_device_rdo.argtypes = [vp, C.c_int64, C.c_int64, C.c_double, C.c_uint32, C.c_uint32,
+                                           C.c_int, C.c_uint32, C.c_uint32, vp, C.c_size_t, vp, vp]
+        L.ep_encode_device_rdo.restype = C.c_int
         _lib = L
     return _lib
 
@@ -309,31 +316,50 @@ class DeviceEncoded:
     coding: str = "standard"
 
 
+def encode_device_rdo_workspace_size(rows: int, cols: int, target_bpp: float, V: int = 0,
+                                     route: str = "direct", candidates: int = 5) -> int:
+    n = C.c_size_t()
+    _check(lib().ep_encode_device_rdo_workspace_size(rows, cols, float(target_bpp), V, ROUTES[route],
+                                                     candidates, C.byref(n)))
+    return n.value
+
+
 def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "direct",
-                  workspace=None, stream=None, coding: str = "standard") -> DeviceEncoded:
+                  workspace=None, stream=None, coding: str = "standard", candidates: int = 0,
+                  sweeps: int = 0) -> DeviceEncoded:
     """Compress a float32 device tensor [rows, cols] with ep_encode_device.
 
     The container matches the host compressor's byte for byte; its arrays are
     left on W's device, ready for decode_tensor / decode_batch.  coding selects
     a Table 4 ablation ("pooled", "direct_z8") on the same points and scales.
+    candidates > 0 runs ep_encode_device_rdo instead (the per-row
+    rate-distortion refinement with that many resolutions per row and
+    `sweeps` sweeps; standard coding only).
     """
     from .encoder import EncodedInfo
     torch = _torch()
     if W.dtype != torch.float32 or W.dim() != 2 or not W.is_cuda:
         raise ValueError("W must be a 2-D float32 device tensor")
+    if candidates and coding != "standard":
+        raise ValueError("the refinement uses the standard coding")
     W = W.contiguous()
     R, Cc = W.shape
     dev = W.device
     if workspace is None:
-        workspace = torch.empty(encode_device_workspace_size(R, Cc, target_bpp, V, route),
-                                dtype=torch.uint8, device=dev)
+        n = (encode_device_rdo_workspace_size(R, Cc, target_bpp, V, route, candidates) if candidates
+             else encode_device_workspace_size(R, Cc, target_bpp, V, route))
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sp = C.c_void_p(stream.cuda_stream)
     info = EncodedInfo()
-    _check(lib().ep_encode_device(W.data_ptr() if W.numel() else None, R, Cc, float(target_bpp), V, b,
-                                  ROUTES[route], CODINGS[coding], workspace.data_ptr(), workspace.numel(),
-                                  sp, C.byref(info)))
+    wp = W.data_ptr() if W.numel() else None
+    if candidates:
+        _check(lib().ep_encode_device_rdo(wp, R, Cc, float(target_bpp), V, b, ROUTES[route], candidates, sweeps,
+                                          workspace.data_ptr(), workspace.numel(), sp, C.byref(info)))
+    else:
+        _check(lib().ep_encode_device(wp, R, Cc, float(target_bpp), V, b, ROUTES[route], CODINGS[coding],
+                                      workspace.data_ptr(), workspace.numel(), sp, C.byref(info)))
     T, nw, nf = info.num_tiles, int(info.payload_words), info.num_freqs
     rs = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
     qs = torch.empty(max(R, 1), dtype=torch.float32, device=dev) if route != "direct" else None
@@ -354,6 +380,7 @@ def encode_device(W, target_bpp: float, V: int = 0, b: int = 0, route: str = "di
 
 ep_encode_device = encode_device
 ep_encode_device_workspace_size = encode_device_workspace_size
+ep_encode_device_rdo_workspace_size = encode_device_rdo_workspace_size
 
 
 def convert_f32(y, dtype: str, stream=None):

@@ -321,20 +321,24 @@ __global__ __launch_bounds__(256) void z8_kernel(int32_t* __restrict__ fields, u
 
 // Per-row sequential passes: lane l of wave 0 owns row r0 + l and adds in
 // column order; all four waves stage the next chunk of kRowChunk columns of
-// the block's 64 rows (and, for the refit, their fields) through registers
+// the block's 64 rows (and, with fields, their fields) through registers
 // into the other half of a double buffer while wave 0 works on the current
-// one.  kRefit = false: sums[r] = sum of w^2.  kRefit = true: least-squares
-// row scale <W_r, sX_r> / <sX_r, sX_r>, X_r rebuilt from the fields.
-template <bool kRefit>
+// one.  kSumSq: sums[r] = sum of w^2.  kRefit: least-squares row scale
+// <W_r, sX_r> / <sX_r, sX_r>, X_r rebuilt from the fields.  kDistortion:
+// sums[r] = sum of (w - y)^2 with y = fp32(x * fp32(s * row_scales[r])), the
+// decoded value.
+enum RowPass : int { kSumSq = 0, kRefit = 1, kDistortion = 2 };
+template <int kMode>
 __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__ Wq, int64_t rows, int64_t cols,
                                                       const int32_t* __restrict__ fields, uint64_t stride,
                                                       double s, double* __restrict__ sums,
                                                       float* __restrict__ row_scales) {
+  constexpr bool kFieldsIn = kMode != kSumSq;
   constexpr int kVec = kRowChunk / 8;                       // vectors per row per chunk
   constexpr int kW4 = kRowBlock * kRowChunk / 4 / 256;      // float4 loads per thread per chunk
-  constexpr int kF = kRefit ? kFields * kRowBlock * kVec / 256 : 1;   // field loads per thread
+  constexpr int kF = kFieldsIn ? kFields * kRowBlock * kVec / 256 : 1;   // field loads per thread
   __shared__ float wt[2][kRowBlock][kRowChunk + 1];
-  __shared__ int32_t ft[2][kRefit ? kFields : 1][kRowBlock][kRefit ? kVec + 1 : 1];
+  __shared__ int32_t ft[2][kFieldsIn ? kFields : 1][kRowBlock][kFieldsIn ? kVec + 1 : 1];
   const int tid = threadIdx.x;
   const int64_t r0 = int64_t(blockIdx.x) * kRowBlock;
   const int nrow = int(std::min<int64_t>(kRowBlock, rows - r0));
@@ -352,7 +356,7 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
       if (row < nrow && 4 * c4 < nc)
         wreg[k] = *reinterpret_cast<const float4*>(Wq + (r0 + row) * cols + c0 + 4 * c4);
     }
-    if (kRefit) {
+    if (kFieldsIn) {
       const int nv = nc / 8;
       const uint64_t j0 = uint64_t(c0) / 8;
 #pragma unroll
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
       wt[buf][row][4 * c4 + 2] = wreg[k].z;
       wt[buf][row][4 * c4 + 3] = wreg[k].w;
     }
-    if (kRefit) {
+    if (kFieldsIn) {
 #pragma unroll
       for (int k = 0; k < kF; ++k) {
         const int f = k >> 2, rem = tid + 256 * (k & 3), row = rem >> 4, v = rem & 15;
@@ -381,6 +385,8 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
   };
 
   double acc = 0.0, num = 0.0, den = 0.0;
+  // the decoded multiplier fp32(s * r) of the row (distortion pass)
+  const float gs = kMode == kDistortion && tid < nrow ? float(s) * row_scales[r0 + tid] : 0.0f;
   gload(0);
   lstore(0);
   __syncthreads();
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
     const int nc = int(std::min<int64_t>(kRowChunk, cols - int64_t(ch) * kRowChunk));
     if (ch + 1 < nchunks) gload(ch + 1);
     if (tid < nrow) {
-      if (!kRefit) {
+      if (kMode == kSumSq) {
         for (int q = 0; q < nc; ++q) {
           const double w = double(wt[buf][tid][q]);
           acc += w * w;
@@ -408,9 +414,15 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
           x2[7] = 2 * z8 + c;
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            const double sx = s * (double(x2[q]) * 0.5);
-            num += double(wt[buf][tid][8 * v + q]) * sx;
-            den += sx * sx;
+            if (kMode == kRefit) {
+              const double sx = s * (double(x2[q]) * 0.5);
+              num += double(wt[buf][tid][8 * v + q]) * sx;
+              den += sx * sx;
+            } else {
+              const float y = float(x2[q]) * 0.5f * gs;
+              const double e = double(wt[buf][tid][8 * v + q]) - double(y);
+              acc += e * e;
+            }
           }
         }
       }
@@ -419,8 +431,111 @@ __global__ __launch_bounds__(256) void row_pass_kernel(const float* __restrict__
     __syncthreads();
   }
   if (tid < nrow) {
-    if (!kRefit) sums[r0 + tid] = acc;
-    else row_scales[r0 + tid] = den > 0.0 ? float(num / den) : 0.0f;
+    if (kMode == kRefit) row_scales[r0 + tid] = den > 0.0 ? float(num / den) : 0.0f;
+    else sums[r0 + tid] = acc;
+  }
+}
+
+// Per-row rate of a set of candidate fields under a model (per-row
+// refinement): block (r, k) adds the costs of row r's symbols in candidate k
+// (planes of `stride` at cand + k * kFields * stride).  Costs are integers
+// (units of 2^-16 bit), so the sum is exact in any order.  A value outside a
+// table's range costs `miss`.
+struct CostArgs {
+  int32_t minv[kTables];
+  uint32_t A[kTables];
+  uint32_t base[kTables];
+  int64_t miss;
+};
+
+__global__ __launch_bounds__(256) void rate_kernel(const int32_t* __restrict__ cand, uint64_t stride,
+                                                  uint64_t per_row, CostArgs ca, const int64_t* __restrict__ cost,
+                                                  uint32_t K, int64_t* __restrict__ rate) {
+  const uint64_t r = blockIdx.x;
+  const uint32_t k = blockIdx.y;
+  const int32_t* f0 = cand + uint64_t(k) * kFields * stride;
+  int64_t acc = 0;
+  for (uint64_t j = threadIdx.x; j < per_row; j += blockDim.x) {
+    const uint64_t g = r * per_row + j;
+    const int c = f0[g];
+    {
+      const int64_t i = c;
+      acc += cost[ca.base[0] + i];
+    }
+#pragma unroll
+    for (int f = 1; f < kFields; ++f) {
+      const int t = 1 + 2 * (f - 1);
+      const int32_t mn = sel(c, ca.minv[t], ca.minv[t + 1]);
+      const uint32_t A = c ? ca.A[t + 1] : ca.A[t];
+      const uint32_t b0 = c ? ca.base[t + 1] : ca.base[t];
+      const int64_t i = int64_t(f0[uint64_t(f) * stride + g]) - mn;
+      acc += (i >= 0 && i < int64_t(A)) ? cost[b0 + i] : ca.miss;
+    }
+  }
+  __shared__ int64_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (int(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) rate[uint64_t(k) * gridDim.x + r] = red[0];
+}
+
+// Gather each row's selected candidate into `fields` and take the per-table
+// ranges like quantize_kernel (lo[k] = min, lo[17 + k] = -max).
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ cand, uint64_t stride,
+                                                    uint64_t nvec, uint64_t per_row,
+                                                    const int32_t* __restrict__ choice,
+                                                    int32_t* __restrict__ fields, int32_t* __restrict__ ranges) {
+  int32_t lo[16], nhi[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    lo[k] = INT32_MAX;
+    nhi[k] = INT32_MAX;
+  }
+  for (uint64_t g = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; g < nvec;
+       g += uint64_t(gridDim.x) * blockDim.x) {
+    const int32_t* src = cand + uint64_t(choice[g / per_row]) * kFields * stride;
+    int32_t fl[kFields];
+#pragma unroll
+    for (int f = 0; f < kFields; ++f) {
+      fl[f] = src[uint64_t(f) * stride + g];
+      fields[uint64_t(f) * stride + g] = fl[f];
+    }
+    const int c = fl[0];
+#pragma unroll
+    for (int f = 1; f < kFields; ++f) {
+      const int k0 = 2 * (f - 1);
+      if (c) {
+        lo[k0 + 1] = min(lo[k0 + 1], fl[f]);
+        nhi[k0 + 1] = min(nhi[k0 + 1], -fl[f]);
+      } else {
+        lo[k0] = min(lo[k0], fl[f]);
+        nhi[k0] = min(nhi[k0], -fl[f]);
+      }
+    }
+  }
+  __shared__ int32_t red[4][32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    int32_t a = lo[k], b = nhi[k];
+    for (int o = 32; o > 0; o >>= 1) {
+      a = min(a, __shfl_xor(a, o));
+      b = min(b, __shfl_xor(b, o));
+    }
+    if (lane == 0) {
+      red[wv][k] = a;
+      red[wv][16 + k] = b;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    int32_t m = red[0][threadIdx.x];
+    for (int w = 1; w < 4; ++w) m = min(m, red[w][threadIdx.x]);
+    const int k = 1 + (threadIdx.x & 15);
+    if (m != INT32_MAX) atomicMin(&ranges[threadIdx.x < 16 ? k : kTables + k], m);
   }
 }
 
@@ -642,7 +757,7 @@ class DeviceEncoder {
     Wq_ = Wq;
     norms_.assign(size_t(std::max<int64_t>(S_.rows, 1)), 0.0);
     if (S_.rows > 0) {
-      row_pass_kernel<false><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
+      row_pass_kernel<kSumSq><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
           Wq, S_.rows, S_.cols, nullptr, 0, 0.0, at<double>(L_.sums), nullptr);
       check(hipGetLastError(), "row_pass_kernel");
       check(hipMemcpyAsync(norms_.data(), at<double>(L_.sums), size_t(S_.rows) * 8, hipMemcpyDeviceToHost, st_),
@@ -658,8 +773,10 @@ class DeviceEncoder {
             "upload sample");
   }
 
-  // Quantise (sampled rows, or all rows) and read the table ranges back.
-  Stats quantize(bool sampled, double s) {
+  // Quantise (sampled rows, or all rows) and read the table ranges back;
+  // the fields go to `dst` (a K-candidate buffer) instead of the main planes
+  // when given.
+  Stats quantize(bool sampled, double s, int32_t* dst = nullptr) {
     const uint64_t nq = sampled ? uint64_t(sample_.size()) * uint64_t(S_.per_row) : S_.nvec;
     nq_ = nq;
     Stats st;
@@ -676,21 +793,98 @@ class DeviceEncoder {
           "clear ranges");
     quantize_kernel<<<grid_for(nq, 256, 2048), 256, 0, st_>>>(Wq_, S_.cols, at<double>(L_.norms),
                                                                sampled ? at<int64_t>(L_.sample) : nullptr, nq, s,
-                                                               at<int32_t>(L_.fields), fields_stride(),
+                                                               dst ? dst : at<int32_t>(L_.fields), fields_stride(),
                                                                at<int32_t>(L_.ranges));
     check(hipGetLastError(), "quantize_kernel");
-    int32_t rg[2 * kTables];
-    check(hipMemcpyAsync(rg, at<int32_t>(L_.ranges), sizeof(rg), hipMemcpyDeviceToHost, st_), "copy ranges");
-    check(hipStreamSynchronize(st_), "quantize");
-    for (int k = 1; k < kTables; ++k) {
-      const int32_t mn = rg[k], mx = rg[kTables + k] == INT32_MAX ? INT32_MIN : -rg[kTables + k];
-      const bool has = mn <= mx;
-      st.minv[k] = has ? mn : 0;
-      st.A[k] = has ? uint32_t(int64_t(mx) - int64_t(mn) + 1) : 0u;
+    return read_ranges("quantize");
+  }
+
+  // Per-row refinement (paper section 3.5, appendix C.2): candidates at
+  // rho_k * s, their row scales and distortions, then `sweeps` rounds of
+  // model update and selection under the baseline's rate.  Leaves the
+  // selected fields in the main planes and returns their ranges; raises b
+  // if the selected fields need it, or keeps the baseline's fields if even
+  // 2^15 does not hold them.
+  Stats rdo(float s, uint32_t& b, uint32_t K, uint32_t sweeps, size_t ext) {
+    rdo_ext_ = ext;
+    const size_t R = size_t(S_.rows), N = size_t(S_.nvec);
+    int32_t* cand = at<int32_t>(ext);
+    const size_t cand_bytes = align256(size_t(K) * kFields * N * 4);
+    float* rsc = at<float>(ext + cand_bytes);
+    double* dist = at<double>(ext + cand_bytes + align256(size_t(K) * R * 4));
+    int64_t* rate = at<int64_t>(ext + cand_bytes + align256(size_t(K) * R * 4) + align256(size_t(K) * R * 8));
+    int32_t* choice = at<int32_t>(ext + cand_bytes + align256(size_t(K) * R * 4) + 2 * align256(size_t(K) * R * 8));
+    int64_t* cost = at<int64_t>(ext + cand_bytes + align256(size_t(K) * R * 4) + 2 * align256(size_t(K) * R * 8) +
+                                align256(R * 4));
+    const std::vector<double> rho = rdo_ratios(K);
+    const int row_blocks = int((S_.rows + kRowBlock - 1) / kRowBlock);
+    for (uint32_t k = 0; k < K; ++k) {
+      int32_t* fk = cand + size_t(k) * kFields * N;
+      quantize(false, double(s) * rho[k], fk);
+      row_pass_kernel<kRefit><<<row_blocks, 256, 0, st_>>>(Wq_, S_.rows, S_.cols, fk, fields_stride(), double(s),
+                                                          nullptr, rsc + size_t(k) * R);
+      row_pass_kernel<kDistortion><<<row_blocks, 256, 0, st_>>>(Wq_, S_.rows, S_.cols, fk, fields_stride(),
+                                                               double(s), dist + size_t(k) * R,
+                                                               rsc + size_t(k) * R);
+      check(hipGetLastError(), "candidate row passes");
     }
-    st.minv[0] = 0;
-    st.A[0] = 2;
-    bases(st);
+    std::vector<double> dk(size_t(K) * R), D(size_t(K) * R);
+    check(hipMemcpyAsync(dk.data(), dist, dk.size() * 8, hipMemcpyDeviceToHost, st_), "copy distortions");
+    check(hipStreamSynchronize(st_), "candidates");
+    for (size_t r = 0; r < R; ++r)
+      for (uint32_t k = 0; k < K; ++k) D[r * K + k] = dk[size_t(k) * R + r];
+    std::vector<int32_t> sel(R, 0);
+    std::vector<int64_t> rk(size_t(K) * R), Rt(size_t(K) * R);
+    int64_t budget = -1;
+    for (uint32_t sw = 0; sw < sweeps; ++sw) {
+      const Stats st = gather(sel, choice);
+      // the model: the selected fields' tables at the smallest precision >= b holding them
+      uint32_t bm = b;
+      for (int k = 1; k < kTables; ++k)
+        while (st.A[k] > (1u << bm) && bm < 15) ++bm;
+      bool fits = true;
+      for (int k = 1; k < kTables; ++k) fits = fits && st.A[k] <= (1u << bm);
+      if (!fits) break;
+      const std::vector<uint64_t> cnt = counts(st);
+      std::vector<int64_t> ct(std::max<uint32_t>(st.sum, 1u), 0);
+      CostArgs ca;
+      ca.miss = int64_t(65536) * int64_t(bm);
+      bool ok = true;
+      for (int k = 0; k < kTables && ok; ++k) {
+        ca.minv[k] = st.minv[k];
+        ca.A[k] = st.A[k];
+        ca.base[k] = st.base[k];
+        if (st.A[k] == 0) continue;
+        std::vector<uint16_t> f(st.A[k]);
+        ok = ep_common::normalize_table(cnt.data() + st.base[k], st.A[k], bm, f.data()) == 0;
+        for (uint32_t i = 0; ok && i < st.A[k]; ++i)
+          ct[st.base[k] + i] = f[i] ? std::llround(65536.0 * (double(bm) - std::log2(double(f[i])))) : ca.miss;
+      }
+      if (!ok) break;
+      check(hipMemcpyAsync(cost, ct.data(), ct.size() * 8, hipMemcpyHostToDevice, st_), "upload costs");
+      rate_kernel<<<dim3(uint32_t(R), K), 256, 0, st_>>>(cand, fields_stride(), uint64_t(S_.per_row), ca, cost, K,
+                                                         rate);
+      check(hipGetLastError(), "rate_kernel");
+      check(hipMemcpyAsync(rk.data(), rate, rk.size() * 8, hipMemcpyDeviceToHost, st_), "copy rates");
+      check(hipStreamSynchronize(st_), "rates");
+      for (size_t r = 0; r < R; ++r)
+        for (uint32_t k = 0; k < K; ++k) Rt[r * K + k] = rk[size_t(k) * R + r];
+      if (budget < 0) {
+        budget = 0;
+        for (size_t r = 0; r < R; ++r) budget += Rt[r * K + size_t(sel[r])];
+      }
+      const double lam = rdo_penalty(D, Rt, R, K, budget);
+      rdo_select(D, Rt, R, K, lam, &sel);
+    }
+    Stats st = gather(sel, choice);
+    uint32_t bf = b;
+    uint32_t amax = max_alphabet(st);
+    while (amax > (1u << bf) && bf < 15) ++bf;
+    if (amax > (1u << bf)) {
+      std::fill(sel.begin(), sel.end(), 0);
+      return gather(sel, choice);
+    }
+    b = bf;
     return st;
   }
 
@@ -755,7 +949,7 @@ class DeviceEncoder {
     I.vectors_per_tile = S_.V;
     I.num_tiles = uint32_t(S_.T);
     if (S_.rows > 0) {
-      row_pass_kernel<true><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
+      row_pass_kernel<kRefit><<<int((S_.rows + kRowBlock - 1) / kRowBlock), 256, 0, st_>>>(
           Wq_, S_.rows, S_.cols, at<int32_t>(L_.fields), fields_stride(), double(s), nullptr, at<float>(L_.rscale));
       check(hipGetLastError(), "row_pass_kernel refit");
     }
@@ -866,6 +1060,98 @@ class DeviceEncoder {
  private:
   uint64_t fields_stride() const { return std::max<uint64_t>(S_.nvec, 1); }
 
+  Stats read_ranges(const char* what) {
+    Stats st;
+    int32_t rg[2 * kTables];
+    check(hipMemcpyAsync(rg, at<int32_t>(L_.ranges), sizeof(rg), hipMemcpyDeviceToHost, st_), "copy ranges");
+    check(hipStreamSynchronize(st_), what);
+    for (int k = 1; k < kTables; ++k) {
+      const int32_t mn = rg[k], mx = rg[kTables + k] == INT32_MAX ? INT32_MIN : -rg[kTables + k];
+      const bool has = mn <= mx;
+      st.minv[k] = has ? mn : 0;
+      st.A[k] = has ? uint32_t(int64_t(mx) - int64_t(mn) + 1) : 0u;
+    }
+    st.minv[0] = 0;
+    st.A[0] = 2;
+    bases(st);
+    return st;
+  }
+
+  // Copy every row's chosen candidate into the main planes.
+  Stats gather(const std::vector<int32_t>& sel, int32_t* choice) {
+    nq_ = S_.nvec;
+    check(hipMemcpyAsync(choice, sel.data(), sel.size() * 4, hipMemcpyHostToDevice, st_), "upload choices");
+    check(hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(at<int32_t>(L_.ranges)), INT32_MAX, 2 * kTables, st_),
+          "clear ranges");
+    gather_kernel<<<grid_for(S_.nvec, 256, 2048), 256, 0, st_>>>(
+        at<int32_t>(rdo_ext_), fields_stride(), S_.nvec, uint64_t(S_.per_row), choice, at<int32_t>(L_.fields),
+        at<int32_t>(L_.ranges));
+    check(hipGetLastError(), "gather_kernel");
+    return read_ranges("gather");
+  }
+
+  // Nested candidate ratios: start at 1 and repeatedly split the widest of
+  // the log-scale intervals between 0.70, 1 and 1.45 at its midpoint
+  // (ties: the lower interval).
+  static std::vector<double> rdo_ratios(uint32_t K) {
+    std::vector<std::pair<double, double>> iv = {{std::log(0.70), 0.0}, {0.0, std::log(1.45)}};
+    std::vector<double> rho;
+    if (K) rho.push_back(1.0);
+    while (rho.size() < K) {
+      size_t w = 0;
+      for (size_t i = 1; i < iv.size(); ++i)
+        if (iv[i].second - iv[i].first > iv[w].second - iv[w].first) w = i;
+      const double mid = 0.5 * (iv[w].first + iv[w].second);
+      rho.push_back(std::exp(mid));
+      iv.insert(iv.begin() + long(w) + 1, {mid, iv[w].second});
+      iv[w].second = mid;
+    }
+    return rho;
+  }
+
+  // Each row's argmin_k D + lam * R (R in 2^-16 bit; ties to the lower k); returns the total rate.
+  static int64_t rdo_select(const std::vector<double>& D, const std::vector<int64_t>& R, size_t rows, uint32_t K,
+                            double lam, std::vector<int32_t>* sel) {
+    int64_t total = 0;
+    for (size_t r = 0; r < rows; ++r) {
+      uint32_t best = 0;
+      double jb = D[r * K] + lam * (double(R[r * K]) / 65536.0);
+      for (uint32_t k = 1; k < K; ++k) {
+        const double j = D[r * K + k] + lam * (double(R[r * K + k]) / 65536.0);
+        if (j < jb) {
+          jb = j;
+          best = k;
+        }
+      }
+      if (sel) (*sel)[r] = int32_t(best);
+      total += R[r * K + best];
+    }
+    return total;
+  }
+
+  // The smallest penalty (doubling from sum D / sum R, then 60 bisection
+  // steps) whose choices fit the budget; 0 if the least-distortion choices fit.
+  static double rdo_penalty(const std::vector<double>& D, const std::vector<int64_t>& R, size_t rows, uint32_t K,
+                            int64_t budget) {
+    if (rdo_select(D, R, rows, K, 0.0, nullptr) <= budget) return 0.0;
+    double sd = 0.0, sr = 0.0;
+    for (size_t r = 0; r < rows; ++r) {
+      sd += D[r * K];
+      sr += double(R[r * K]) / 65536.0;
+    }
+    double hi = (sd > 0.0 && sr > 0.0) ? sd / sr : 1e-30, lo = 0.0;
+    for (int it = 0; it < 200 && rdo_select(D, R, rows, K, hi, nullptr) > budget; ++it) {
+      lo = hi;
+      hi *= 2.0;
+    }
+    for (int i = 0; i < 60; ++i) {
+      const double mid = 0.5 * (lo + hi);
+      if (rdo_select(D, R, rows, K, mid, nullptr) > budget) lo = mid;
+      else hi = mid;
+    }
+    return hi;
+  }
+
   static void bases(Stats& st) {
     uint32_t acc = 0;
     for (int k = 0; k < kTables; ++k) {
@@ -885,7 +1171,19 @@ class DeviceEncoder {
   std::vector<int64_t> sample_;
   std::vector<uint16_t> freqs_;
   std::vector<uint32_t> tab_;
+
+ public:
+  size_t rdo_ext_ = 0;      // workspace offset of the refinement's candidate fields
 };
+
+// Workspace beyond the compressor's own layout for the per-row refinement:
+// K candidates' fields, row scales, distortions and rates, the choices and
+// the model's cost table.
+size_t rdo_extra_bytes(const Shape& S, uint32_t K) {
+  const size_t R = size_t(std::max<int64_t>(S.rows, 1)), N = size_t(std::max<uint64_t>(S.nvec, 1));
+  return align256(size_t(K) * kFields * N * 4) + align256(size_t(K) * R * 4) + 2 * align256(size_t(K) * R * 8) +
+         align256(R * 4) + align256(size_t(S.nbins) * 8);
+}
 
 }  // namespace
 
@@ -901,9 +1199,15 @@ int ep_encode_device_workspace_size(int64_t rows, int64_t cols, double target_bp
   return EP_OK;
 }
 
-int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
-                     uint32_t prob_bits, int route, int coding, void* workspace, size_t ws_bytes, void* stream,
-                     ep_encoded_info* info) {
+}  // extern "C"
+
+namespace {
+
+// The compressor: argument checks, Algorithm 1 with escalation, optionally
+// the per-row refinement (K > 1 and sweeps > 0), then the container.
+int encode_impl(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
+                uint32_t prob_bits, int route, int coding, uint32_t K, uint32_t sweeps, void* workspace,
+                size_t ws_bytes, void* stream, ep_encoded_info* info) {
   if (!info) return ep_record_error(EP_ERR_INVALID_ARG, "info is NULL");
   if (coding < EP_CODING_STANDARD || coding > EP_CODING_DIRECT_Z8)
     return ep_record_error(EP_ERR_INVALID_ARG, "coding must be an ep_coding");
@@ -915,8 +1219,11 @@ int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_b
   if (rc != EP_OK) return ep_record_error(rc, "invalid tensor shape, target, tile size or route");
   uint32_t b = prob_bits ? prob_bits : ep_common::default_prob_bits(target_bpp);
   if (b < 9 || b > 15) return ep_record_error(EP_ERR_INVALID_ARG, "prob_bits must be in [9, 15]");
+  const bool refine = K > 1 && sweeps > 0 && S.nvec > 0;
+  if (refine && rows > int64_t(INT32_MAX)) return ep_record_error(EP_ERR_UNSUPPORTED, "too many rows to refine");
   const Layout L = make_layout(S);
-  if (!workspace || ws_bytes < L.bytes) return ep_record_error(EP_ERR_WORKSPACE, "workspace too small");
+  const size_t need = L.bytes + (refine ? rdo_extra_bytes(S, K) : 0);
+  if (!workspace || ws_bytes < need) return ep_record_error(EP_ERR_WORKSPACE, "workspace too small");
   if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return ep_record_error(EP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
@@ -948,6 +1255,7 @@ int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_b
       }
       break;
     }
+    if (refine) st = E.rdo(s, b, K, sweeps, L.bytes);
     rc = E.finish(s, b, st, coding, I);
     if (rc != EP_OK) return ep_record_error(rc, "a table could not be normalised or the payload is too long");
   } catch (const HipFailure& f) {
@@ -955,6 +1263,36 @@ int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_b
   }
   *info = I;
   return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
+                     uint32_t prob_bits, int route, int coding, void* workspace, size_t ws_bytes, void* stream,
+                     ep_encoded_info* info) {
+  return encode_impl(W, rows, cols, target_bpp, vectors_per_tile, prob_bits, route, coding, 0, 0, workspace,
+                     ws_bytes, stream, info);
+}
+
+int ep_encode_device_rdo_workspace_size(int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
+                                        int route, uint32_t candidates, size_t* bytes) {
+  if (!bytes) return ep_record_error(EP_ERR_INVALID_ARG, "bytes is NULL");
+  if (candidates < 1 || candidates > 32) return ep_record_error(EP_ERR_INVALID_ARG, "candidates must be in [1, 32]");
+  Shape S;
+  const int rc = make_shape(rows, cols, target_bpp, vectors_per_tile, route, S);
+  if (rc != EP_OK) return ep_record_error(rc, "invalid tensor shape, target, tile size or route");
+  *bytes = make_layout(S).bytes + rdo_extra_bytes(S, candidates);
+  return EP_OK;
+}
+
+int ep_encode_device_rdo(const float* W, int64_t rows, int64_t cols, double target_bpp, uint32_t vectors_per_tile,
+                         uint32_t prob_bits, int route, uint32_t candidates, uint32_t sweeps, void* workspace,
+                         size_t ws_bytes, void* stream, ep_encoded_info* info) {
+  if (candidates < 1 || candidates > 32) return ep_record_error(EP_ERR_INVALID_ARG, "candidates must be in [1, 32]");
+  return encode_impl(W, rows, cols, target_bpp, vectors_per_tile, prob_bits, route, EP_CODING_STANDARD, candidates,
+                     sweeps, workspace, ws_bytes, stream, info);
 }
 
 int ep_encode_device_emit(const void* workspace, const ep_encoded_info* info, float* row_scales,

@@ -58,6 +58,36 @@ int ep_encode_device(const float* W, int64_t rows, int64_t cols, double target_b
                      void* workspace, size_t ws_bytes, void* stream, ep_encoded_info* info);
 
 /*
+ * Device workspace bytes ep_encode_device_rdo needs with `candidates`
+ * resolutions per row: the ep_encode_device_workspace_size() bytes, then the
+ * candidates' fields (about 36 bytes per 8 weights each), their row scales,
+ * distortions and rates (20 bytes per row each), the choices and a cost
+ * table.  Host-only arithmetic; candidates in [1, 32].
+ */
+int ep_encode_device_rdo_workspace_size(int64_t rows, int64_t cols, double target_bpp,
+                                        uint32_t vectors_per_tile, int route, uint32_t candidates,
+                                        size_t* bytes);
+
+/*
+ * ep_encode_device (standard coding) with the optional per-row
+ * rate-distortion refinement of the paper's section 3.5 and appendix C.2
+ * (Algorithm 2): after the scale search, every row may take one of
+ * `candidates` resolutions rho_k * s (rho_1 = 1, nested bisections of
+ * [0.70, 1.45] in log scale) with its own fitted row scale; `sweeps` rounds
+ * each rebuild the shared probability model from the selected fields and
+ * reselect all rows under one rate penalty, keeping the baseline's total code
+ * length.  The container is decoded like any other (only the encoder's
+ * choices change), and ep_encode_device_emit reads it from the same
+ * workspace.  candidates = 1 or sweeps = 0 give ep_encode_device's container.
+ * The result is byte-identical to the CPU reference refinement.  Synchronises
+ * `stream` like ep_encode_device, a few more times per sweep.
+ */
+int ep_encode_device_rdo(const float* W, int64_t rows, int64_t cols, double target_bpp,
+                         uint32_t vectors_per_tile, uint32_t prob_bits, int route,
+                         uint32_t candidates, uint32_t sweeps, void* workspace, size_t ws_bytes,
+                         void* stream, ep_encoded_info* info);
+
+/*
  * Copy the result of the last ep_encode_device on `workspace` (described by
  * its *info) into caller device buffers, enqueued asynchronously on `stream`;
  * any pointer may be NULL.  Sizes: row_scales and route_scales [rows] (the

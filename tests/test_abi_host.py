@@ -199,3 +199,28 @@ def test_convert_argument_errors():
     assert L.ep_convert_f32(fake, fake, 8, 100, None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_convert_f32(fake, fake, 8, 4, None) == ep.EP_ERR_INVALID_ARG   # FP32 needs no rounding
     assert L.ep_convert_f32(fake, fake, 0, 0, None) == ep.EP_OK
+
+
+def test_device_refinement_workspace_size_and_argument_errors():
+    import ctypes as C
+    from dit_weight_compression_amd import encoder as enc
+    L = ep.lib()
+    n = C.c_size_t()
+    for K in (0, 33):
+        assert L.ep_encode_device_rdo_workspace_size(64, 256, 3.0, 0, 0, K, C.byref(n)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device_rdo_workspace_size(64, 60, 3.0, 0, 0, 5, C.byref(n)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device_rdo_workspace_size(64, 256, 3.0, 0, 0, 5, None) == ep.EP_ERR_INVALID_ARG
+    base = ep.encode_device_workspace_size(1000, 1024, 3.0)
+    sizes = [ep.encode_device_rdo_workspace_size(1000, 1024, 3.0, candidates=K) for K in (1, 5, 9)]
+    nvec = 1000 * 1024 // 8
+    # every candidate keeps its own fields (36 B per vector)
+    assert sizes[0] >= base + 36 * nvec and sizes[1] - sizes[0] >= 4 * 36 * nvec and sizes[2] > sizes[1]
+    info = enc.EncodedInfo()
+    fake = C.c_void_p(1 << 40)
+    need = ep.encode_device_rdo_workspace_size(8, 64, 3.0, candidates=5)
+    for K in (0, 33):
+        assert L.ep_encode_device_rdo(fake, 8, 64, 3.0, 0, 0, 0, K, 1, fake, need, None,
+                                      C.byref(info)) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_encode_device_rdo(fake, 8, 64, 3.0, 0, 0, 0, 5, 1, fake, need - 1, None,
+                                  C.byref(info)) == ep.EP_ERR_WORKSPACE
+    assert L.ep_encode_device_rdo(fake, 8, 64, 3.0, 0, 0, 0, 5, 1, fake, need, None, None) == ep.EP_ERR_INVALID_ARG

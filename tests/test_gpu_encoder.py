@@ -178,3 +178,32 @@ def test_device_encoder_table4_codings(coding, target):
     out = _decode_ok(d, "lattice2x")
     std = oracle.encode(W, target)
     assert np.array_equal(out.cpu().numpy(), oracle.decode(std, "lattice2x")[0])
+
+
+RDO_CASES = [
+    # (label, rows, cols, seed, target, K, sweeps, route)
+    ("3bpp K5 one sweep", 256, 512, 3, 3.0, 5, 1, "direct"),
+    ("3bpp K9 two sweeps", 192, 768, 51, 3.0, 9, 2, "direct"),
+    ("4bpp K3 three sweeps, ragged rows", 77, 264, 52, 4.0, 3, 3, "direct"),
+    ("2bpp K5 fp8 route", 128, 512, 53, 2.0, 5, 1, "fp8"),
+    ("6bpp K4 int8 route", 96, 384, 54, 6.0, 4, 2, "int8"),
+    ("K1 is the baseline", 64, 256, 55, 3.0, 1, 1, "direct"),
+    ("no sweep is the baseline", 64, 256, 56, 3.0, 5, 0, "direct"),
+    ("layer-width rows 1024 x 3840, 3bpp K5", 1024, 3840, 57, 3.0, 5, 1, "direct"),
+]
+
+
+@pytest.mark.parametrize("label, rows, cols, seed, target, K, sweeps, route", RDO_CASES)
+def test_device_refinement_matches_oracle(label, rows, cols, seed, target, K, sweeps, route):
+    W = synthgen.student_t_weights(rows, cols, seed).numpy()
+    print(f"[rdo] {label}", flush=True)
+    ref = oracle.encode_rdo(W, target, K=K, sweeps=sweeps, route=route)
+    d = ep.encode_device(torch.from_numpy(W).cuda(), target, route=route, candidates=K, sweeps=sweeps)
+    _assert_same_container(ref, d, label)
+    out = _decode_ok(d, "bf16" if route == "direct" else route)
+    ref_out, _ = oracle.decode(ref, "bf16" if route == "direct" else route)
+    view = {"direct": torch.int16, "fp8": torch.uint8, "int8": torch.int8}[route]
+    got = out.view(view).cpu().numpy()
+    assert np.array_equal(got.view(ref_out.dtype), ref_out), label
+    if K == 1 or sweeps == 0:
+        _assert_same_container(oracle.encode(W, target, route=route), d, label + " (baseline)")
