@@ -536,6 +536,52 @@ def coding_ablations(reps: int):
     print(json.dumps({"coding_ablations": {"layer": [spec.rows, spec.cols], "points": rows}}), flush=True)
 
 
+def rdo_sweep(reps: int):
+    """The per-row refinement on the reference layer shape at 3 bpp (the
+    paper's appendix A.4 setting): stored rate, weight error and device
+    compression time against the candidate count K (one sweep) and the sweep
+    count (K = 5).  The baseline row is ep_encode_device without refinement.
+    Every container is decoded by the GPU decoder with all tiles OK; the
+    weight error is that of the decoded FP32 weights.
+    """
+    import torch
+
+    import dit_weight_compression_amd as ep
+    import synthgen
+
+    spec = synthgen.workload("ref_layer_10240x3840_4bpp_bf16")[0]
+    W = spec.weights(device="cuda:0")
+    target = 3.0
+    ws = torch.empty(ep.encode_device_rdo_workspace_size(spec.rows, spec.cols, target, candidates=20),
+                     dtype=torch.uint8, device="cuda:0")
+    w64 = W.double()
+    wn = float((w64 * w64).sum())
+    configs = [(0, 0)] + [(K, 1) for K in (1, 3, 5, 9, 20)] + [(5, sw) for sw in (0, 2, 4, 8)]
+    rows = []
+    for K, sweeps in configs:
+        enc = lambda: ep.encode_device(W, target, workspace=ws, candidates=K, sweeps=sweeps)  # noqa: E731
+        d = enc()
+        p = d.packed
+        y, st = ep.decode_tensor(p, "fp32", with_status=True)
+        torch.cuda.synchronize()
+        ok = bool((st[: p.T] == 0).all())
+        err = float(((y.double() - w64) ** 2).sum()) / wn
+        del y
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            enc()
+            torch.cuda.synchronize()
+            ts.append(1e3 * (time.perf_counter() - t0))
+        rows.append({"candidates": K, "sweeps": sweeps, "b": p.b, "stored_bpp": 8.0 * p.stored_bytes / p.numel,
+                     "weight_error_pct": 100.0 * err ** 0.5, "encode_ms_median": sorted(ts)[len(ts) // 2],
+                     "tiles_ok": ok})
+        log(json.dumps(rows[-1]))
+        del d, p
+    print(json.dumps({"rdo": {"layer": [spec.rows, spec.cols], "target_bpp": target, "points": rows}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,7 +606,13 @@ def main():
                     help="only time the device compressor per layer beside the host compressor")
     ap.add_argument("--ablations", action="store_true",
                     help="only measure the Table 4 coding ablations on the reference layer shape")
+    ap.add_argument("--rdo", action="store_true",
+                    help="only measure the per-row refinement on the reference layer shape at 3 bpp")
     args = ap.parse_args()
+
+    if args.rdo:
+        rdo_sweep(max(min(args.steps, 5), 1))
+        return
 
     if args.ablations:
         coding_ablations(max(args.steps, 1))
