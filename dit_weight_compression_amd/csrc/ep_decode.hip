@@ -100,6 +100,8 @@ struct alignas(16) DevTensor {
   uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
   uint32_t slow_rows;        // set by the table build when some row's g/2 is inexact: use g
   uint32_t f8z8;             // 1: field 8 holds z8 (no parity reduction), 0: it holds m
+  uint32_t chunk0;           // index of the tensor's first chunk in the schedule
+  uint32_t tpc;              // tiles per chunk of the tensor's launch group
   uint64_t payload_words;
   const float* row_scales;
   float* rowv;               // workspace: per row the pair (g/2, g), g = fp32(scale * row scale)
@@ -137,9 +139,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---------------------------------------------------------------- table build
 // One block per (coordinate table, tensor): cumulative frequencies by a block
 // scan, then the slot -> symbol map by a binary search per slot.
-__global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens) {
+__global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens, Chunk* __restrict__ chunks,
+                                                          uint32_t row_blocks) {
   DevTensor& T = tens[blockIdx.y];
   if (T.T == 0) return;
+  if (blockIdx.x >= 16 + row_blocks) {
+    // the tensor's entries of the tile schedule, 1024 per block
+    const uint32_t nch = (T.T + T.tpc - 1) / T.tpc;
+    const uint32_t j0 = (blockIdx.x - 16 - row_blocks) * 1024u;
+    const uint32_t j1 = min(nch, j0 + 1024u);
+    for (uint32_t j = j0 + threadIdx.x; j < j1; j += 256u) chunks[T.chunk0 + j] = Chunk{blockIdx.y, j * T.tpc};
+    return;
+  }
   if (blockIdx.x >= 16) {
     // per-row multipliers, 1024 rows per block: (2 z + c) * (g / 2) equals
     // (z + c/2) * g exactly whenever g / 2 is exact; the pair (g/2, g) is
@@ -936,9 +947,10 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
-  std::vector<unsigned char> host(L.tab_off.empty() ? L.total : L.tab_off[0], 0);
+  // only the descriptors travel; the build kernel writes the tile schedule
+  std::vector<unsigned char> host(L.chunk_off, 0);
   DevTensor* ht = reinterpret_cast<DevTensor*>(host.data() + L.tens_off);
-  Chunk* hc = reinterpret_cast<Chunk*>(host.data() + L.chunk_off);
+  uint32_t chunk_blocks = 0;
   char* wsb = static_cast<char*>(workspace);
   // chunks are grouped by (table placement, output kind); each group is one
   // launch with its own chunk size
@@ -1024,19 +1036,25 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.kvals[17] = ((kpar >> 1) & 1u) << psh;
     D.empty_mask = em;
     D.kpar = kpar;
+    // the tensor's chunks (consecutive in its group's range) are written by the table build
     const uint32_t tpc = P->groups[L.group[i]].tiles_per_chunk;
-    for (uint32_t t0 = 0; t0 < d.num_tiles; t0 += tpc)
-      hc[group_pos[L.group[i]]++] = Chunk{uint32_t(i), t0};
+    const uint32_t nch = uint32_t((uint64_t(d.num_tiles) + tpc - 1) / tpc);
+    D.tpc = tpc;
+    D.chunk0 = uint32_t(group_pos[L.group[i]]);
+    group_pos[L.group[i]] += nch;
+    chunk_blocks = std::max<uint32_t>(chunk_blocks, (nch + 1023u) / 1024u);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
+  hipError_t e = host.empty() ? hipSuccess
+                              : hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
   if (n > 0) {
     uint64_t max_rows = 1;
     for (int i = 0; i < n; ++i) max_rows = std::max<uint64_t>(max_rows, uint64_t(descs[i].rows));
     const uint32_t row_blocks = uint32_t((max_rows + 1023) / 1024);
-    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks, n), dim3(256), 0, st,
-                       reinterpret_cast<DevTensor*>(wsb + L.tens_off));
+    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks + chunk_blocks, n), dim3(256), 0, st,
+                       reinterpret_cast<DevTensor*>(wsb + L.tens_off), reinterpret_cast<Chunk*>(wsb + L.chunk_off),
+                       row_blocks);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
   }

@@ -207,3 +207,16 @@ def test_device_refinement_matches_oracle(label, rows, cols, seed, target, K, sw
     assert np.array_equal(got.view(ref_out.dtype), ref_out), label
     if K == 1 or sweeps == 0:
         _assert_same_container(oracle.encode(W, target, route=route), d, label + " (baseline)")
+
+
+@pytest.mark.timeout(300)
+def test_device_refinement_full_reference_layer():
+    # the reference layer shape at the paper's refinement setting (3 bpp, K = 5, one sweep),
+    # against the CPU oracle's refinement
+    w = synthgen.workload("ref_layer_10240x3840_4bpp_bf16")[0]
+    W = w.weights().numpy()
+    print(f"[rdo] reference layer {W.shape}", flush=True)
+    ref = oracle.encode_rdo(W, 3.0, K=5, sweeps=1)
+    d = ep.encode_device(torch.from_numpy(W).cuda(), 3.0, candidates=5, sweeps=1)
+    _assert_same_container(ref, d, "reference layer, refinement")
+    _decode_ok(d)
