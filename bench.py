@@ -230,7 +230,19 @@ def cpu_baseline(hosts, dtype: str, budget_s: float, threads: int):
     return {"value": wn / sn / 1e9, "unit": "Gweights/s", "cores": threads, "kind": "oracle",
             "sample": f"first {nn} tensor(s) of the workload ({wn} weights) decoded to {dtype} by the "
                       f"CPU oracle on {threads} threads over tile ranges in {sn:.1f}s; one thread: "
-                      f"{n1} tensor(s), {w1} weights in {s1:.1f}s = {w1 / s1 / 1e9:.4f} Gweights/s"}
+                      f"{n1} tensor(s), {w1} weights in {s1:.1f}s = {w1 / s1 / 1e9:.4f} Gweights/s; "
+                      f"host CPU: {_cpu_model()}"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_sha256() -> str:

@@ -9,11 +9,13 @@
 //
 // Mapping: one wave64 decodes two tiles, one per half-wave; lane l of a half
 // owns the tile's rANS state l (the paper assigns one tile per 32-lane warp and
-// one state per lane).  Workgroups of 16 waves are persistent and keep the
-// current tensor's decode tables in LDS; each tile streams its payload words
-// through a small LDS ring.  Renormalisation reads of a half-wave are located
-// with a wave ballot and mbcnt, so the lanes that need a word read consecutive
-// ring positions.  Each lane reconstructs whole 8-wide vectors and writes them
+// one state per lane).  Workgroups of 16 waves are persistent, keep the
+// current tensor's decode tables in LDS and hand out pairs of tiles to their
+// waves through a work counter; each tile streams its payload words through a
+// small LDS ring.  Renormalisation reads of a half-wave are located with a
+// wave ballot (the popcount of the half's bits below the lane), so the lanes
+// that need a word read consecutive ring positions.  Each lane reconstructs
+// whole 8-wide vectors and writes them
 // with one 16-byte (BF16) or 8-byte (FP8/INT8) buffer store; the 32 lanes of a
 // half write 512 (256) contiguous bytes.
 #include <hip/hip_runtime.h>
