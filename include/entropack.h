@@ -44,7 +44,8 @@
  * Errors: argument problems are reported synchronously as a negative
  * ep_status before any GPU work is enqueued.  Corrupt streams are reported per
  * tile in the optional tile_status arrays; a corrupt tile's output region is
- * left undefined, but every read stays inside the tile's own payload range.
+ * left undefined, but every read stays inside the tensor's payload buffer and
+ * every write inside the tensor's output.
  */
 #ifndef ENTROPACK_H
 #define ENTROPACK_H
