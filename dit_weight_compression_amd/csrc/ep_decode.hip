@@ -104,6 +104,8 @@ struct alignas(16) DevTensor {
   uint32_t f8z8;             // 1: field 8 holds z8 (no parity reduction), 0: it holds m
   uint32_t chunk0;           // index of the tensor's first chunk in the schedule
   uint32_t tpc;              // tiles per chunk of the tensor's launch group
+  uint32_t direct;           // packed layouts: entries hold the value 2 z + c - 2 dmin (see kvals)
+  int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
   uint64_t payload_words;
   const float* row_scales;
   float* rowv;               // workspace: per row the pair (g/2, g), g = fp32(scale * row scale)
@@ -117,7 +119,9 @@ struct alignas(16) DevTensor {
   // packed layouts, value constants as fp32 bit patterns, indexed by table t:
   // t < 14: 2^23 + 2^22 + [f = 2^11] - (2 min_t + c) (wide: 2^23 + 2^22 - min_t),
   // t = 14, 15: 2^23 + 2^22 - (4 min_t + c); t = 16, 17: parity of the minima
-  // of z1..z7 in coset t - 16, at the symbol's bit position
+  // of z1..z7 in coset t - 16, at the symbol's bit position.  Direct entries:
+  // t = 18 + (f - 1) for f = 1..7: 2^23 + 2^22 - 2 dmin[f]; t = 25: the field-8
+  // constant; t = 26: the multiplier (+-2, or 0) of the parity bit for field 8
   uint32_t kvals[32];
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
@@ -246,7 +250,14 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     }
     if (is_packed(tl)) {
       const uint32_t e = cums[lo];
-      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | (lo << (tl == kTabPacked ? 23 : 22));
+      // the entry's top bits: the symbol index, or (direct entries) the value
+      // 2 z + c (4 m + c for field 8) relative to the field's smaller minimum
+      uint32_t top = lo << (tl == kTabPacked ? 23 : 22);
+      if (tl == kTabPacked && T.direct) {
+        const int32_t d = int32_t(lo) + mn - T.dmin[field];
+        top = uint32_t((field < 8 || T.f8z8 ? 2 * d : 4 * d) + int32_t(c)) << 22;
+      }
+      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | top;
     } else if (tl == kTabNarrow) {
       lut8[j] = uint8_t(lo);
     } else {
@@ -403,6 +414,18 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   // packed tables: lane i < 18 holds value constant i (see DevTensor::kvals);
   // a lane fetches the one for its coset with ds_bpermute
   const uint32_t kreg = is_packed(TL) ? ((const EP_GLOBAL uint32_t*)T.kvals)[l] : 0u;
+  // direct entries (packed layout): uniform value constants, no per-lane fetch
+  constexpr bool kDirectable = TL == kTabPacked;
+  const bool direct = kDirectable && T.direct != 0;
+  const uint32_t fw = kWide || direct ? 11u : 12u;           // width of f in the entry
+  float kd[7] = {0, 0, 0, 0, 0, 0, 0}, k8d = 0.0f;
+  int32_t m8d = 0;
+  if (kDirectable) {
+#pragma unroll
+    for (int f = 0; f < 7; ++f) kd[f] = __builtin_bit_cast(float, T.kvals[18 + f]);
+    k8d = __builtin_bit_cast(float, T.kvals[25]);
+    m8d = int32_t(T.kvals[26]);
+  }
 
   // the chunk held in registers is always the one starting at word F of the half
   u32x2 pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane, 0, 0);
@@ -505,10 +528,27 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         const uint32_t toff = (uint32_t(2 * (f - 1) - (hi ? 8 : 0)) << B) * 4u;
         const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << 2) & (MASK << 2)) | (hi ? lbh : lbl)) + toff);
         q = x >> B;
-        x = __umul24(__builtin_amdgcn_ubfe(e, 11, kWide ? 11 : 12), q) + (e & 0x7FFu);
+        x = __umul24(__builtin_amdgcn_ubfe(e, 11, fw), q) + (e & 0x7FFu);
         ev[f] = e;
         EP_RENORM();
       }
+      if (kDirectable && direct) {
+        // direct entries: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 +
+        // (2 z + c - 2 dmin), and one constant per field (the same for both
+        // cosets) turns it into 2 z + c.  Bit 23 of an entry is the parity of
+        // z - dmin, so the XOR of z1..z7's entries gives the parity of their
+        // sum up to the parity of the minima, which the field-8 constant and
+        // multiplier absorb: 2 z8 + c = (4 (m - dmin8) + c) + 2 par + 4 dmin8.
+#pragma unroll
+        for (int f = 1; f <= 7; ++f)
+          vv[f] = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22)) - kd[f - 1];
+        const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+            __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
+            __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96), ev[7], 0x96);
+        par = __builtin_amdgcn_ubfe(x3, 23, pw);
+        const int32_t u8 = __mul24(int32_t(par), m8d) + int32_t(__builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[8], 22));
+        vv[8] = __builtin_bit_cast(float, u8) - k8d;
+      } else {
       // value of z_f.  Packed: 0x4B400000 | (e >> 22) is the float
       // 2^23 + 2^22 + 2 s (+1 when f = 2^11), and the per-table constant turns
       // it into 2 z + c.  Wide: the same bits give 2^23 + 2^22 + s, the
@@ -535,6 +575,7 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
       const uint32_t u8 = ((ev[8] >> kSymShift) << sh8) + ((par << 1) | 0x4B400000u);
       const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
       vv[8] = __builtin_bit_cast(float, u8) - k8;
+      }
     } else {
       uint32_t sv[9];
       const uint32_t lb = c ? M : 0u;                    // coset offset inside each table pair
@@ -1036,6 +1077,40 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     const uint32_t psh = wide ? 22 : 23;
     D.kvals[16] = (kpar & 1u) << psh;
     D.kvals[17] = ((kpar >> 1) & 1u) << psh;
+    // direct entries (packed layout): each field's values over both cosets
+    // must fit the entry's 10 top bits as 2 (z - dmin) + c (4 (m - dmin) + c
+    // for field 8), and every f must fit 11 bits
+    {
+      bool direct = layout_of(L.variant[i]) == kTabPacked;
+      int64_t dsum = 0;
+      const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
+      for (int f = 1; f <= 8; ++f) {
+        int64_t mn = 0, mx = -1;
+        for (int c = 0; c < 2; ++c) {
+          const int k = 1 + 2 * (f - 1) + c;
+          if (d.alphabet[k] == 0) continue;
+          if (d.prob_bits == 11 && d.alphabet[k] == 1) direct = false;   // f = 2^11
+          const int64_t lo = d.min_offset[k], hi = lo + d.alphabet[k] - 1;
+          if (mx < mn) mn = lo, mx = hi;
+          else mn = std::min(mn, lo), mx = std::max(mx, hi);
+        }
+        if (mx < mn) mn = mx = 0;
+        if ((f < 8 ? 2 : k8) * (mx - mn) + 1 > 1023) direct = false;
+        D.dmin[f] = int32_t(mn);
+        if (f < 8) {
+          dsum += mn;
+          const float kf = float(12582912 - 2 * mn);
+          std::memcpy(&D.kvals[18 + f - 1], &kf, 4);
+        }
+      }
+      D.dmin[0] = 0;
+      // field 8: 2 z8 + c = v8 + k8 dmin8 + 2 par (coded m), par = p ^ parity(sum of dmin1..7)
+      const int64_t kd8 = (d.field8 == EP_FIELD8_Z8) ? 0 : (dsum & 1);
+      const float k8f = float(12582912 - k8 * D.dmin[8] - 2 * kd8);
+      std::memcpy(&D.kvals[25], &k8f, 4);
+      D.kvals[26] = uint32_t(d.field8 == EP_FIELD8_Z8 ? 0 : (kd8 ? -2 : 2));
+      D.direct = direct ? 1u : 0u;
+    }
     D.empty_mask = em;
     D.kpar = kpar;
     // the tensor's chunks (consecutive in its group's range) are written by the table build
