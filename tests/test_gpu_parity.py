@@ -372,3 +372,15 @@ def test_large_batch_runs_and_work_counter():
             ref, _ = oracle.decode(ct, "bf16")
             assert np.array_equal(_gpu_out_numpy(outs[i], "bf16"), ref), f"rep {rep} tensor {i}"
             assert np.all(sts[i].cpu().numpy()[: ct.T] == 0)
+
+
+@pytest.mark.parametrize("s", [8.0, 12.0])
+def test_packed_direct_and_symbol_entries(s):
+    """b = 11 packed tables in both entry forms on the same data: at s = 8 every
+    table has several symbols (direct-value entries); at s = 12 some coordinate
+    tables hold one symbol (f = 2^11 needs 12 bits, so the symbol form is used)."""
+    W = synthgen.student_t_weights(128, 512, 61).numpy()
+    ct = oracle.encode_fixed_scale(W, s, V=64, b=11)
+    assert ct.b == 11
+    assert (1 in ct.alphabet[1:].tolist()) == (s == 12.0)
+    _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8"), label=f"s={s}")
