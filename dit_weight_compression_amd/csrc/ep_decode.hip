@@ -120,8 +120,9 @@ struct alignas(16) DevTensor {
   // t < 14: 2^23 + 2^22 + [f = 2^11] - (2 min_t + c) (wide: 2^23 + 2^22 - min_t),
   // t = 14, 15: 2^23 + 2^22 - (4 min_t + c); t = 16, 17: parity of the minima
   // of z1..z7 in coset t - 16, at the symbol's bit position.  Direct entries:
-  // t = 18 + (f - 1) for f = 1..7: 2^23 + 2^22 - 2 dmin[f]; t = 25: the field-8
-  // constant; t = 26: the multiplier (+-2, or 0) of the parity bit for field 8
+  // t = 18 + (f - 1) for f = 1..7: -(2^23 + 2^22 - 2 dmin[f]); t = 25: the
+  // negated field-8 constant; t = 26: the multiplier (+-2, or 0) of the parity
+  // bit for field 8
   uint32_t kvals[32];
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
@@ -414,7 +415,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   // packed tables: lane i < 18 holds value constant i (see DevTensor::kvals);
   // a lane fetches the one for its coset with ds_bpermute
   const uint32_t kreg = is_packed(TL) ? ((const EP_GLOBAL uint32_t*)T.kvals)[l] : 0u;
-  // direct entries (packed layout): uniform value constants, no per-lane fetch
+  // direct entries (packed layout): uniform value constants (stored negated:
+  // the adds cannot be merged with the symbol form's subtractions, which keeps
+  // the constants in scalar registers), no per-lane fetch
   constexpr bool kDirectable = TL == kTabPacked;
   const bool direct = kDirectable && T.direct != 0;
   const uint32_t fw = kWide || direct ? 11u : 12u;           // width of f in the entry
@@ -541,13 +544,13 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         // multiplier absorb: 2 z8 + c = (4 (m - dmin8) + c) + 2 par + 4 dmin8.
 #pragma unroll
         for (int f = 1; f <= 7; ++f)
-          vv[f] = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22)) - kd[f - 1];
+          vv[f] = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22)) + kd[f - 1];
         const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
             __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
             __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96), ev[7], 0x96);
         par = __builtin_amdgcn_ubfe(x3, 23, pw);
         const int32_t u8 = __mul24(int32_t(par), m8d) + int32_t(__builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[8], 22));
-        vv[8] = __builtin_bit_cast(float, u8) - k8d;
+        vv[8] = __builtin_bit_cast(float, u8) + k8d;
       } else {
       // value of z_f.  Packed: 0x4B400000 | (e >> 22) is the float
       // 2^23 + 2^22 + 2 s (+1 when f = 2^11), and the per-table constant turns
@@ -618,14 +621,14 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo4), rO, ob, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi4), rO, ob + 16u, 0, 0);
     } else {
-      float y[8];
-      if (!slow_rows) {
+      // slow rows: rv is g and 2 z + c is halved first (exactly)
+      if (slow_rows) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], rv);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(vv[i + 1], 0.5f), rv);
+        for (int i = 1; i <= 8; ++i) vv[i] = __fmul_rn(vv[i], 0.5f);
       }
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], rv);
       if (OK == kOutBF16) {
         const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                          pack_bf16x2(y[6], y[7])};
@@ -1099,14 +1102,14 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
         D.dmin[f] = int32_t(mn);
         if (f < 8) {
           dsum += mn;
-          const float kf = float(12582912 - 2 * mn);
+          const float kf = -float(12582912 - 2 * mn);
           std::memcpy(&D.kvals[18 + f - 1], &kf, 4);
         }
       }
       D.dmin[0] = 0;
       // field 8: 2 z8 + c = v8 + k8 dmin8 + 2 par (coded m), par = p ^ parity(sum of dmin1..7)
       const int64_t kd8 = (d.field8 == EP_FIELD8_Z8) ? 0 : (dsum & 1);
-      const float k8f = float(12582912 - k8 * D.dmin[8] - 2 * kd8);
+      const float k8f = -float(12582912 - k8 * D.dmin[8] - 2 * kd8);
       std::memcpy(&D.kvals[25], &k8f, 4);
       D.kvals[26] = uint32_t(d.field8 == EP_FIELD8_Z8 ? 0 : (kd8 ? -2 : 2));
       D.direct = direct ? 1u : 0u;
