@@ -281,9 +281,21 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 // INT8 code: round half to even, clamp to [-128, 127] (v_med3_f32).
-__device__ __forceinline__ uint32_t int8_rne(float y) {
-  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(y), -128.0f, 127.0f);
-  return uint32_t(int32_t(r)) & 0xFFu;
+// INT8 (or, with kUnsigned, UINT8 = INT8 + 128) codes of four values, bytes in
+// order.  Clamping to [-128, 127] first is the same as rounding first (the
+// bounds are integers); adding 2^23 + 2^22 (+ 128) then rounds to nearest
+// even and leaves the two's-complement code (or the offset code) in the low
+// byte of the sum's bit pattern, and byte permutes gather the four low bytes.
+template <bool kUnsigned>
+__device__ __forceinline__ uint32_t int8_codes4(float a, float b, float c, float d) {
+  constexpr float kMagic = kUnsigned ? 12583040.0f : 12582912.0f;
+  const uint32_t ta = __float_as_uint(__builtin_amdgcn_fmed3f(a, -128.0f, 127.0f) + kMagic);
+  const uint32_t tb = __float_as_uint(__builtin_amdgcn_fmed3f(b, -128.0f, 127.0f) + kMagic);
+  const uint32_t tc = __float_as_uint(__builtin_amdgcn_fmed3f(c, -128.0f, 127.0f) + kMagic);
+  const uint32_t td = __float_as_uint(__builtin_amdgcn_fmed3f(d, -128.0f, 127.0f) + kMagic);
+  const uint32_t lo = __builtin_amdgcn_perm(tb, ta, 0x0C0C0400u);   // a.b0, b.b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(td, tc, 0x0C0C0400u);   // c.b0, d.b0, 0, 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -646,10 +658,9 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
         const u32x2 w = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       } else {
-        // INT8 codes; UINT8 adds the offset 128, i.e. flips each byte's top bit
-        const uint32_t off = OK == kOutUINT8 ? 0x80808080u : 0u;
-        const u32x2 w = {(int8_rne(y[0]) | (int8_rne(y[1]) << 8) | (int8_rne(y[2]) << 16) | (int8_rne(y[3]) << 24)) ^ off,
-                         (int8_rne(y[4]) | (int8_rne(y[5]) << 8) | (int8_rne(y[6]) << 16) | (int8_rne(y[7]) << 24)) ^ off};
+        // INT8 codes; UINT8 adds the offset 128
+        const u32x2 w = {int8_codes4<OK == kOutUINT8>(y[0], y[1], y[2], y[3]),
+                         int8_codes4<OK == kOutUINT8>(y[4], y[5], y[6], y[7])};
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
       }
     }
@@ -750,9 +761,7 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
     } else if (OK == kOutFP8) {
       reinterpret_cast<uint32_t*>(out)[q] = pack_fp8x4(v.x, v.y, v.z, v.w);
     } else {
-      const uint32_t off = OK == kOutUINT8 ? 0x80808080u : 0u;
-      reinterpret_cast<uint32_t*>(out)[q] =
-          (int8_rne(v.x) | (int8_rne(v.y) << 8) | (int8_rne(v.z) << 16) | (int8_rne(v.w) << 24)) ^ off;
+      reinterpret_cast<uint32_t*>(out)[q] = int8_codes4<OK == kOutUINT8>(v.x, v.y, v.z, v.w);
     }
   }
 }
