@@ -280,7 +280,6 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return uint32_t(w);
 }
 
-// INT8 code: round half to even, clamp to [-128, 127] (v_med3_f32).
 // INT8 (or, with kUnsigned, UINT8 = INT8 + 128) codes of four values, bytes in
 // order.  Clamping to [-128, 127] first is the same as rounding first (the
 // bounds are integers); adding 2^23 + 2^22 (+ 128) then rounds to nearest
