@@ -60,7 +60,13 @@ constexpr size_t kMaxLds = 160 * 1024;
 //             2^b, read from the workspace through the caches.
 //   hybrid    (b = 11, 12 with alphabets too large for the above): the
 //             workspace format, with the u16 slot maps (64 / 128 KB) staged in
-//             LDS and the per-symbol entries read through the caches.
+//             LDS and the per-symbol entries read through the caches.  At
+//             b = 11, two per-slot arrays follow it (64 KB each) and, staged in
+//             LDS together, replace both lookups when every frequency of the
+//             tensor is below 128 (the build checks) and every value fits 16
+//             bits (the host checks): u16 f | (slot - cum) << 7 | (parity of
+//             z) << 15, and the i16 value 2 z + c (4 m + c for m) of the
+//             slot's symbol.  (At b = 12 the two arrays would need 256 KB.)
 enum TabLayout : int { kTabPacked = 0, kTabNarrow = 1, kTabWorkspace = 2, kTabPackedWide = 3, kTabHybrid = 4 };
 enum Variant : uint32_t {
   kVarP9 = 0, kVarP10, kVarP11, kVarW10, kVarW11, kVarN12, kVarH11, kVarH12, kVarWs, kNumVariants
@@ -82,9 +88,19 @@ __host__ __device__ constexpr size_t lut_bytes_of(int tl, uint32_t b) {
 __host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
   return lut_bytes_of(tl, b) + 2 * size_t(16) * stride_of(tl, b) * 4;
 }
+// hybrid layout at b = 11: byte offset of the per-slot entry maps after the
+// workspace format; the per-slot values follow them
+__host__ __device__ constexpr bool has_split(int tl, uint32_t b) { return tl == kTabHybrid && b == 11; }
+__host__ __device__ constexpr size_t split_off_of(uint32_t b) { return table_bytes_of(kTabWorkspace, b); }
+__host__ __device__ constexpr size_t split_bytes_of(uint32_t b) { return (size_t(16) << b) * 4; }
+__host__ __device__ constexpr size_t storage_bytes_of(int tl, uint32_t b) {
+  return table_bytes_of(tl, b) + (has_split(tl, b) ? split_bytes_of(b) : 0);
+}
 // bytes of a tensor's tables that the decode kernel stages in LDS
 __host__ __device__ constexpr size_t lds_table_bytes_of(int tl, uint32_t b) {
-  return tl == kTabWorkspace ? 0 : tl == kTabHybrid ? lut_bytes_of(tl, b) : table_bytes_of(tl, b);
+  return tl == kTabWorkspace ? 0
+       : tl == kTabHybrid ? (has_split(tl, b) ? split_bytes_of(b) : lut_bytes_of(tl, b))
+       : table_bytes_of(tl, b);
 }
 
 // Device-side view of one tensor (lives in the workspace).
@@ -105,6 +121,7 @@ struct alignas(16) DevTensor {
   uint32_t chunk0;           // index of the tensor's first chunk in the schedule
   uint32_t tpc;              // tiles per chunk of the tensor's launch group
   uint32_t direct;           // packed layouts: entries hold the value 2 z + c - 2 dmin (see kvals)
+  uint32_t split;            // hybrid layout: 1 = per-slot entries usable (cleared by the build if some f > 127)
   int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
   uint64_t payload_words;
   const float* row_scales;
@@ -184,7 +201,10 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   const uint32_t A = T.alphabet[k];
   const uint32_t b = T.b;
   const uint32_t M = 1u << b;
+  const bool split = has_split(layout_of(T.variant), b);
   const int tl = storage_of(layout_of(T.variant));
+  uint16_t* fd16 = reinterpret_cast<uint16_t*>(T.tab + split_off_of(b)) + (size_t(t) << b);
+  int16_t* sval = reinterpret_cast<int16_t*>(T.tab + split_off_of(b)) + (size_t(16 + t) << b);
   const uint32_t S = stride_of(tl, b);
   unsigned char* lut8 = T.tab + (size_t(t) << b);
   uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
@@ -206,6 +226,10 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
       if (is_packed(tl)) lut32[j] = 1u << 11;      // f = 1, slot - cum = 0, symbol 0
       else if (tl == kTabNarrow) lut8[j] = 0;
       else lut16[j] = 0;
+      if (split) {
+        fd16[j] = 1;                                // f = 1, slot - cum = 0
+        sval[j] = 0;
+      }
     }
     return;
   }
@@ -241,6 +265,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     __syncthreads();
   }
   // slot j -> largest i with cum_i <= j (a zero-frequency symbol is never chosen)
+  int big = 0;
   for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
     uint32_t lo = 0, hi = A;
     while (hi - lo > 1) {
@@ -263,8 +288,18 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
       lut8[j] = uint8_t(lo);
     } else {
       lut16[j] = uint16_t(lo);
+      if (split) {
+        const uint32_t e = sym[lo];
+        const uint32_t f = e & 0xFFFFu, d = j - ((e >> 16) - (c << b));
+        const uint32_t zp = field < 8 ? (uint32_t(int32_t(lo) + mn) & 1u) : 0u;
+        big |= f > 127u;
+        fd16[j] = uint16_t((f & 0x7Fu) | (d << 7) | (zp << 15));
+        sval[j] = int16_t(val[lo]);                  // |value| < 2^15: checked on the host
+      }
     }
   }
+  // per-slot entries hold f in 7 bits: any larger frequency disables them for the tensor
+  if (__syncthreads_or(big) && threadIdx.x == 0) atomicAnd(&T.split, 0u);
 }
 
 // ---------------------------------------------------------------- container rounding
@@ -347,8 +382,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // Decode the two tiles of one wave (tile0 + 2*wave + half, if that slot is below
 // the chunk's tile count).  BT is the
 // probability precision when known at compile time (0: read T.b), TL the
-// table layout (LDS tables start at LDS address 0), OK the output kind.
-template <int BT, int TL, int OK>
+// table layout (LDS tables start at LDS address 0), OK the output kind, SP
+// (hybrid layout) whether the per-slot entry maps are the ones staged in LDS.
+template <int BT, int TL, int OK, bool SP>
 __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
                                             const unsigned char* __restrict__ lds,
                                             uint16_t* __restrict__ ring) {
@@ -590,6 +626,31 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
       const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
       vv[8] = __builtin_bit_cast(float, u8) - k8;
       }
+    } else if constexpr (SP) {
+      // per-slot entries f | (slot - cum) << 7 | parity << 15 and the slot
+      // symbol's value 2 z + c (i16), both in LDS (b = 11: 64 KB each)
+      static_assert(BT == 11, "per-slot entries are built for b = 11");
+      uint32_t ev[9];
+      uint32_t lbl = c ? (M << 1) : 0u;                  // byte offset of the coset's map
+      asm volatile("" : "+v"(lbl));
+#pragma unroll
+      for (int f = 1; f <= 8; ++f) {
+        const uint32_t toff = (uint32_t(2 * (f - 1)) << B) * 2u;       // at most 57344
+        const uint32_t a = ((x << 1) & (MASK << 1)) | lbl;
+        const uint32_t e = *reinterpret_cast<const uint16_t*>(lds + a + toff);
+        // the values follow the 16 entry maps (64 KB): a second base register
+        const uint32_t av = a | (uint32_t(16) << (B + 1));
+        vv[f] = float(*reinterpret_cast<const int16_t*>(lds + av + toff));
+        q = x >> B;
+        x = __umul24(e & 0x7Fu, q) + __builtin_amdgcn_ubfe(e, 7, 7);
+        ev[f] = e;
+        EP_RENORM();
+      }
+      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
+                                                      __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
+                                                      ev[7], 0x96);
+      par = __builtin_amdgcn_ubfe(x3, 15, pw);
+      vv[8] = vv[8] + float(par << 1);                   // the m values are 4 m + c (z8: 2 z8 + c)
     } else {
       uint32_t sv[9];
       const uint32_t lb = c ? M : 0u;                    // coset offset inside each table pair
@@ -727,10 +788,13 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     const uint32_t npairs = (t_end - ch.tile0 + 1) / 2;
     __syncthreads();                       // every wave is done with the previous run
     if (threadIdx.x == 0) __hip_atomic_store(ctr + ci, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // hybrid layout: the per-slot entry maps when the build kept them, else the slot maps
+    const bool split = has_split(TL, BT) && T.split != 0;
     if (TL != kTabWorkspace) {
-      const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)T.tab;
+      const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)(T.tab + (split ? split_off_of(BT) : 0));
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
-      for (uint32_t i = threadIdx.x; i < uint32_t(kTab / 16u); i += kBlock) dst[i] = src[i];
+      const uint32_t n16 = uint32_t((has_split(TL, BT) && !split ? lut_bytes_of(TL, BT) : kTab) / 16u);
+      for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = src[i];
     }
     __syncthreads();
     // the first pair of each wave is its own index, which spreads a short run
@@ -738,7 +802,12 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     uint32_t pr = threadIdx.x >> 6, nx = 0;
     while (pr < npairs) {
       if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
-      decode_pair<BT, TL, OK>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+      if constexpr (has_split(TL, BT)) {
+        if (split) decode_pair<BT, TL, OK, true>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+        else decode_pair<BT, TL, OK, false>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+      } else {
+        decode_pair<BT, TL, OK, false>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+      }
       pr = __builtin_amdgcn_readfirstlane(nx);
     }
     ci = cn;
@@ -862,7 +931,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     if (ok < 0) return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": unknown output dtype");
     L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
-    L.tab_bytes[i] = table_bytes_of(layout_of(L.variant[i]), d.prob_bits);
+    L.tab_bytes[i] = storage_bytes_of(layout_of(L.variant[i]), d.prob_bits);
     L.max_chunks += (d.num_tiles + 1) / 2;
     L.group_tiles[L.group[i]] += d.num_tiles;
   }
@@ -1121,6 +1190,20 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       std::memcpy(&D.kvals[25], &k8f, 4);
       D.kvals[26] = uint32_t(d.field8 == EP_FIELD8_Z8 ? 0 : (kd8 ? -2 : 2));
       D.direct = direct ? 1u : 0u;
+    }
+    // hybrid at b = 11: per-slot entries when every value 2 z + c (4 m + c) fits
+    // 16 bits; the build clears the flag if some f > 127
+    {
+      bool fits = has_split(layout_of(L.variant[i]), d.prob_bits);
+      const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
+      for (int k = 1; k < kTables && fits; ++k) {
+        if (d.alphabet[k] == 0) continue;
+        const int64_t mul = k >= 15 ? k8 : 2, c = (k - 1) & 1;
+        const int64_t lo = mul * int64_t(d.min_offset[k]) + c;
+        const int64_t hi = mul * (int64_t(d.min_offset[k]) + d.alphabet[k] - 1) + c;
+        fits = lo >= -32768 && hi <= 32767;
+      }
+      D.split = fits ? 1u : 0u;
     }
     D.empty_mask = em;
     D.kpar = kpar;

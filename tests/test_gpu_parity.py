@@ -317,17 +317,28 @@ def test_container_rounding_matches_oracle_at_every_boundary():
                                  f"(bits {v[i:i+1].view(np.uint32)[0]:#010x}) gpu={got[i]} oracle={ref[i]}")
 
 
-@pytest.mark.parametrize("target, b, outliers", [(7.0, 11, 0.002), (8.0, 12, 0.0), (7.0, 12, 0.0)])
-def test_hybrid_layout_large_alphabets(target, b, outliers):
-    # b = 11 with alphabets above 1024 and b = 12 above 256: the u16 slot maps sit
-    # in LDS, the per-symbol entries are read from the workspace
-    W = synthgen.student_t_weights(192, 2048, 101 if b == 11 else 90 + b, bf16=True,
-                                   outlier_frac=outliers).numpy()
+def _max_coordinate_freq(ct) -> int:
+    return max(int(ct.freqs[ct.freq_base[k]:ct.freq_base[k] + ct.alphabet[k]].max())
+               for k in range(1, 17) if ct.alphabet[k])
+
+
+@pytest.mark.parametrize("target, b, outliers, seed, split", [
+    (7.0, 11, 0.002, 101, True),      # every f < 128: per-slot entries and values in LDS
+    (6.0, 11, 0.01, 108, False),      # some f >= 128: u16 slot maps in LDS, entries from the workspace
+    (8.0, 12, 0.0, 102, False),       # b = 12: always the slot maps
+    (7.0, 12, 0.0, 102, False),
+])
+def test_hybrid_layout_large_alphabets(target, b, outliers, seed, split):
+    # b = 11 with alphabets above 1024 and b = 12 above 256.  At b = 11 the table
+    # build keeps per-slot entries when every frequency is below 128; otherwise
+    # the decoder reads the u16 slot maps and the per-symbol entries.
+    W = synthgen.student_t_weights(192, 2048, seed, bf16=True, outlier_frac=outliers).numpy()
     ct = oracle.encode(W, target, b=b)
-    amax = int(ct.alphabet[1:].max())
-    print(f"[hybrid] target={target} b={ct.b} A={amax}", flush=True)
+    amax, fmax = int(ct.alphabet[1:].max()), _max_coordinate_freq(ct)
+    print(f"[hybrid] target={target} b={ct.b} A={amax} max f={fmax}", flush=True)
     assert ct.b == b and amax > (1024 if b == 11 else 256)
-    _check_parity(ct, kinds=("lattice2x", "bf16", "fp8", "uint8"), label=f"hybrid b={b} A={amax}")
+    assert (b == 11 and fmax < 128) == split
+    _check_parity(ct, kinds=("lattice2x", "bf16", "fp8", "uint8"), label=f"hybrid b={b} A={amax} f<={fmax}")
 
 
 def test_rows_whose_half_multiplier_is_inexact():
