@@ -41,6 +41,11 @@ def _ref_bits(ref: np.ndarray, kind: str) -> np.ndarray:
     return ref.view(np.uint32) if kind == "fp32" else ref
 
 
+def _max_coordinate_freq(ct) -> int:
+    return max(int(ct.freqs[ct.freq_base[k]:ct.freq_base[k] + ct.alphabet[k]].max())
+               for k in range(1, 17) if ct.alphabet[k])
+
+
 def _check_parity(ct, kinds=("bf16", "lattice2x"), label=""):
     p = ep.PackedTensor.from_arrays(ct)
     for kind in kinds:
@@ -160,16 +165,19 @@ def test_deterministic_repeat_and_workspace_reuse():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("target, b, outliers, rows, cols", [
-    (4.0, 11, 0.0, 64, 512),        # packed tables
-    (4.0, 12, 0.0, 64, 512),        # narrow tables
-    (8.0, 12, 0.002, 96, 2048),     # hybrid tables (A > 256 at b = 12)
-    (8.0, 13, 0.002, 96, 2048),     # global tables
+@pytest.mark.parametrize("target, b, outliers, rows, cols, seed, V", [
+    (4.0, 11, 0.0, 64, 512, 11, 64),        # packed tables
+    (4.0, 12, 0.0, 64, 512, 11, 64),        # narrow tables
+    (8.0, 12, 0.002, 96, 2048, 11, 64),     # hybrid tables (A > 256 at b = 12)
+    (7.0, 11, 0.002, 192, 2048, 101, 0),    # hybrid at b = 11 with per-slot entries (A > 1024, f < 128)
+    (8.0, 13, 0.002, 96, 2048, 11, 64),     # global tables
 ])
-def test_corrupt_streams_flagged_like_oracle(target, b, outliers, rows, cols):
-    W = synthgen.student_t_weights(rows, cols, 11, outlier_frac=outliers).numpy()
-    ct = oracle.encode(W, target, V=64, b=b)
+def test_corrupt_streams_flagged_like_oracle(target, b, outliers, rows, cols, seed, V):
+    W = synthgen.student_t_weights(rows, cols, seed, outlier_frac=outliers).numpy()
+    ct = oracle.encode(W, target, V=V, b=b)
     print(f"[corrupt] b={ct.b} A={ct.alphabet[1:].max()} T={ct.T}", flush=True)
+    if b == 11 and V == 0:
+        assert ct.alphabet[1:].max() > 1024 and _max_coordinate_freq(ct) < 128
     rng = np.random.default_rng(0)
     pl = ct.payload.copy()
     stt = ct.states.copy()
@@ -315,11 +323,6 @@ def test_container_rounding_matches_oracle_at_every_boundary():
             i = bad[0]
             raise AssertionError(f"{kind}: {bad.size} of {v.size} differ; first y={v[i]!r} "
                                  f"(bits {v[i:i+1].view(np.uint32)[0]:#010x}) gpu={got[i]} oracle={ref[i]}")
-
-
-def _max_coordinate_freq(ct) -> int:
-    return max(int(ct.freqs[ct.freq_base[k]:ct.freq_base[k] + ct.alphabet[k]].max())
-               for k in range(1, 17) if ct.alphabet[k])
 
 
 @pytest.mark.parametrize("target, b, outliers, seed, split", [
