@@ -256,15 +256,19 @@ def decode_batch(packed: Sequence[PackedTensor], dtypes, outs=None, with_status:
     if isinstance(dtypes, str):
         dtypes = [dtypes] * len(packed)
     dev = packed[0].payload.device if packed else torch.device("cuda")
-    if outs is None:
-        outs = alloc_outputs(packed, dtypes, dev)
-    statuses = None
-    if with_status:
-        statuses = [torch.full((max(p.T, 1),), -1, dtype=torch.int32, device=dev) for p in packed]
-    if workspace is None:
-        workspace = torch.empty(workspace_size(packed), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    # Buffers made here are allocated on the launch stream: the caching
+    # allocator then hands their memory only to later work on that stream,
+    # which runs after the decode even when the caller's current stream differs.
+    with torch.cuda.stream(stream):
+        if outs is None:
+            outs = alloc_outputs(packed, dtypes, dev)
+        statuses = None
+        if with_status:
+            statuses = [torch.full((max(p.T, 1),), -1, dtype=torch.int32, device=dev) for p in packed]
+        if workspace is None:
+            workspace = torch.empty(workspace_size(packed), dtype=torch.uint8, device=dev)
     args = BatchArgs(packed, dtypes, outs, statuses, workspace)
     args.call(C.c_void_p(stream.cuda_stream))
     return outs, statuses
@@ -275,13 +279,14 @@ def decode_tensor(p: PackedTensor, dtype: str = "bf16", out=None, with_status: b
     """Decode one tensor with ep_decode_tensor; returns (out, status)."""
     torch = _torch()
     dev = p.payload.device
-    if out is None:
-        out = alloc_outputs([p], [dtype], dev)[0]
-    status = torch.full((max(p.T, 1),), -1, dtype=torch.int32, device=dev) if with_status else None
-    if workspace is None:
-        workspace = torch.empty(workspace_size([p]), dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    with torch.cuda.stream(stream):      # see decode_batch: allocations on the launch stream
+        if out is None:
+            out = alloc_outputs([p], [dtype], dev)[0]
+        status = torch.full((max(p.T, 1),), -1, dtype=torch.int32, device=dev) if with_status else None
+        if workspace is None:
+            workspace = torch.empty(workspace_size([p]), dtype=torch.uint8, device=dev)
     d = p.desc()
     _check(lib().ep_decode_tensor(C.byref(d), DTYPES[dtype], out.data_ptr(),
                                   None if status is None else status.data_ptr(),

@@ -398,3 +398,28 @@ def test_packed_direct_and_symbol_entries(s):
     assert ct.b == 11
     assert (1 in ct.alphabet[1:].tolist()) == (s == 12.0)
     _check_parity(ct, kinds=("bf16", "lattice2x", "fp8", "int8"), label=f"s={s}")
+
+
+def test_decode_on_a_side_stream_keeps_its_buffers():
+    # decode_tensor / decode_batch allocate their workspace (and any outputs and
+    # statuses) on the launch stream.  Work queued at once on the caller's current
+    # stream, allocating blocks of the workspace's size and writing them, must not
+    # get that memory while the decode still reads it.
+    W = synthgen.student_t_weights(3072, 2048, 13, bf16=True).numpy()
+    ct = oracle.encode(W, 4.0)
+    p = ep.PackedTensor.from_arrays(ct)
+    ref, _ = oracle.decode(ct, "bf16")
+    nws = ep.workspace_size([p])
+    side = torch.cuda.Stream()                 # default priority
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out, st = ep.decode_tensor(p, "bf16", with_status=True, stream=side)
+        outs, sts = ep.decode_batch([p, p], "bf16", with_status=True, stream=side)
+        junk = [torch.full((nws,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(16)]
+        junk += [torch.full((max(p.T, 1),), 7, dtype=torch.int32, device="cuda") for _ in range(16)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        for o, s in [(out, st)] + list(zip(outs, sts)):
+            assert np.all(s.cpu().numpy()[: ct.T] == 0)
+            assert np.array_equal(_gpu_out_numpy(o, "bf16"), ref)
+        del junk
