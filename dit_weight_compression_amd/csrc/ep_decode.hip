@@ -31,6 +31,7 @@
 
 // global (not flat) addressing for pointers read from the descriptors
 #define EP_GLOBAL __attribute__((address_space(1)))
+#define EP_LDS __attribute__((address_space(3)))
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -39,10 +40,9 @@ namespace {
 
 constexpr uint32_t kL = 1u << 15;          // lower bound of the state interval
 constexpr int kTables = EP_NUM_TABLES;
-constexpr int kTilesPerWave = 2;
 constexpr int kWavesPerBlock = 16;
 constexpr int kBlock = 64 * kWavesPerBlock;
-constexpr int kTilesPerChunk = kTilesPerWave * kWavesPerBlock;
+constexpr int kMaxChains = 2;                // independent tile pairs a wave decodes together
 constexpr size_t kMaxLds = 160 * 1024;
 
 // ---------------------------------------------------------------- decode tables
@@ -348,18 +348,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // ---------------------------------------------------------------- decode
 // Per-tile payload staging: each half-wave streams its tile's words through an
-// LDS ring of kRingWords, filled kChunkWords at a time (one 8-byte load per
-// lane).  Every vector round issues exactly three memory operations -- the
-// row-scale load, the next ring chunk and the output store -- all as raw
-// buffer operations, whose out-of-range lanes the hardware turns into zero
-// loads and dropped stores.  With a fixed count per round the waits stay
-// precise: waiting for this round's row scale never waits for the chunk in
-// flight behind it.
-constexpr uint32_t kRingWords = 512;
-constexpr uint32_t kChunkWords = 128;
-constexpr uint32_t kRoundWords = 9 * 32;                 // most words one vector round can read
+// LDS ring of kRingWords, filled kChunkWords at a time (one 4-byte load per
+// lane).  Before a round starts, the words its first five fields can read are
+// staged; after field 4 a check makes sure the words the last four fields can
+// read are there too (rarely not: a round reads about a fifth of its worst
+// case).  Every memory operation is a raw buffer operation, whose out-of-range
+// lanes the hardware turns into zero loads and dropped stores; a prefetch at or
+// past the tile's last word gets an out-of-range offset and reads nothing.
+constexpr uint32_t kRingWords = 256;
+constexpr uint32_t kChunkWords = 64;
+constexpr uint32_t kHead0 = 5 * 32;                       // most words fields 0..4 of a round read
+constexpr uint32_t kHead1 = 4 * 32;                       // most words fields 5..8 read
 constexpr uint32_t kRingSlack = kRingWords - kChunkWords; // a chunk fits while fill <= read + slack
-constexpr size_t kRingBytes = size_t(kTilesPerChunk) * kRingWords * sizeof(uint16_t);
+static_assert(kHead0 + kChunkWords <= kRingWords && kHead1 + kChunkWords <= kRingWords,
+              "a staged segment and the chunk being written must fit the ring");
+
+// LDS of the payload rings: every wave holds 2 * CH rings (CH chains of two tiles)
+__host__ __device__ constexpr size_t ring_bytes_of(int ch) {
+  return size_t(kWavesPerBlock) * 2u * size_t(ch) * kRingWords * sizeof(uint16_t);
+}
+constexpr size_t kRingBytesMax = ring_bytes_of(kMaxChains);
 
 enum OutKind : int {
   kOutBF16 = 0, kOutFP8 = 1, kOutINT8 = 2, kOutLattice = 3, kOutFP16 = 4, kOutFP32 = 5, kOutUINT8 = 6,
@@ -379,15 +387,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
-// Decode the two tiles of one wave (tile0 + 2*wave + half, if that slot is below
-// the chunk's tile count).  BT is the
-// probability precision when known at compile time (0: read T.b), TL the
-// table layout (LDS tables start at LDS address 0), OK the output kind, SP
-// (hybrid layout) whether the per-slot entry maps are the ones staged in LDS.
-template <int BT, int TL, int OK, bool SP>
-__device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
-                                            const unsigned char* __restrict__ lds,
-                                            uint16_t* __restrict__ ring) {
+// Decode the 2*CH consecutive tiles tile0 .. tile0 + 2*CH - 1 of one wave (those
+// below tile_end).  Chain c of the wave is the tile pair tile0 + 2c, tile0 + 2c + 1,
+// one tile per half-wave; lane l of a half owns the tile's rANS state l.  The CH
+// chains are independent and advance round by round together: while one
+// chain waits for a table lookup, the other's arithmetic can issue, so a wave
+// exposes less of the LDS latency of its serial per-symbol chain.
+//
+// BT is the probability precision when known at compile time (0: read T.b),
+// TL the table layout (LDS tables start at LDS address 0), OK the output kind,
+// SP (hybrid layout) whether the per-slot entry maps are the ones staged in
+// LDS, CH the number of chains.  `rings` points to this wave's 2*CH rings.
+template <int BT, int TL, int OK, bool SP, int CH>
+__device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
+                                             const unsigned char* __restrict__ lds,
+                                             uint16_t* __restrict__ rings) {
   constexpr bool kWs = TL == kTabWorkspace;
   constexpr bool kHyb = TL == kTabHybrid;
   constexpr bool kGlobalEntries = kWs || kHyb;             // per-symbol entries read from the workspace
@@ -398,50 +412,79 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t half = lane >> 5;
   const uint32_t hs = half << 4;                            // selects this half's packed 16 bits
+  const uint32_t hs32 = half << 5;                          // selects this half's 32 ballot bits
   const uint32_t l = lane & 31u;
-  const uint32_t t = tile0 + half;                          // tile of this half-wave
-  const bool tile_ok = t < tile_end;                        // tile_end <= T.T
+  const uint32_t lane2 = 2u * l;                            // this lane's words inside a chunk
 
-  // ---- per-lane tile start
-  uint32_t n = 0, x = kL, p = 0, pend = 0;
-  bool bad_len = false;
-  if (tile_ok) {
-    const uint64_t first = uint64_t(t) * T.V;
-    n = uint32_t(min(uint64_t(T.V), T.nvec - first));
-    x = ((const EP_GLOBAL uint32_t*)T.states)[size_t(t) * EP_LANES + l];
-    p = ((const EP_GLOBAL uint32_t*)T.offsets)[t];
-    pend = ((const EP_GLOBAL uint32_t*)T.offsets)[t + 1];
-    if (pend < p || pend > T.payload_words) {
-      bad_len = true;
-      n = 0;
-      pend = p;
-    }
-  }
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(T.payload, T.payload_bytes);
   // descriptor fields used inside the round loop, read once: the output
   // stores could alias the descriptor as far as the compiler knows
   const uint32_t vpr = T.vpr;
   const uint32_t out_bytes = T.out_bytes;
+  const uint32_t payload_bytes = T.payload_bytes;
   const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, out_bytes);
   const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 8u);
+  const bool slow_rows = T.slow_rows != 0;
 
-  // ---- per-half-wave uniform state (scalar registers)
-  const uint32_t n0 = __builtin_amdgcn_readlane(n, 0), n1 = __builtin_amdgcn_readlane(n, 32);
-  const uint32_t st0 = __builtin_amdgcn_readlane(p, 0), st1 = __builtin_amdgcn_readlane(p, 32);
-  const uint32_t a00 = st0 & ~3u, a01 = st1 & ~3u;          // 8-byte aligned first word
-  const uint32_t end0 = __builtin_amdgcn_readlane(pend, 0) - a00;
-  const uint32_t end1 = __builtin_amdgcn_readlane(pend, 32) - a01;
-  uint32_t P0 = st0 - a00, P1 = st1 - a01;                  // ring-relative read pointers
-  // the read pointer of this lane's half, kept per lane so that the
-  // renormalisation needs no scalar bookkeeping; P0 / P1 are refreshed from it
-  // once per round for the ring fill
-  uint32_t vP = half ? P1 : P0;
-  const uint32_t hs32 = half << 5;                          // selects this half's 32 ballot bits
-  uint32_t F0 = 0, F1 = 0;                                  // words written to the ring
-  uint64_t empty_err = 0;
-  const uint32_t lane4 = 4u * l;                            // this lane's words inside a chunk
-  const uint32_t chunk_lane = 2u * ((half ? a01 : a00) + lane4);   // byte offset of this lane's part
-  const uint32_t kmax = max((n0 + 31u) >> 5, (n1 + 31u) >> 5);
+  // ---- per-chain tile start.  Uniform values of a chain's two tiles live in
+  // scalar registers; each lane keeps its half's ring read pointer (vP) so
+  // that the renormalisation needs no scalar bookkeeping.
+  uint32_t n[CH], x[CH], vP[CH], F0[CH], F1[CH], end0[CH], end1[CH], n0[CH], n1[CH];
+  uint32_t chunk_lane[CH], pf[CH], g[CH], rowb[CH], col[CH];
+  uint64_t empty_err[CH];
+  bool bad_len[CH], tile_ok[CH];
+  uint32_t kfull = ~0u, kmax = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t t = tile0 + 2u * uint32_t(c) + half;     // tile of this half-wave
+    tile_ok[c] = t < tile_end;                               // tile_end <= T.T
+    uint32_t p = 0, pend = 0;
+    n[c] = 0;
+    x[c] = kL;
+    bad_len[c] = false;
+    if (tile_ok[c]) {
+      const uint64_t first = uint64_t(t) * T.V;
+      n[c] = uint32_t(min(uint64_t(T.V), T.nvec - first));
+      x[c] = ((const EP_GLOBAL uint32_t*)T.states)[size_t(t) * EP_LANES + l];
+      p = ((const EP_GLOBAL uint32_t*)T.offsets)[t];
+      pend = ((const EP_GLOBAL uint32_t*)T.offsets)[t + 1];
+      if (pend < p || pend > T.payload_words) {
+        bad_len[c] = true;
+        n[c] = 0;
+        pend = p;
+      }
+    }
+    n0[c] = __builtin_amdgcn_readlane(n[c], 0);
+    n1[c] = __builtin_amdgcn_readlane(n[c], 32);
+    const uint32_t st0 = __builtin_amdgcn_readlane(p, 0), st1 = __builtin_amdgcn_readlane(p, 32);
+    const uint32_t a00 = st0 & ~1u, a01 = st1 & ~1u;         // 4-byte aligned first word
+    end0[c] = __builtin_amdgcn_readlane(pend, 0) - a00;       // ring-relative word counts
+    end1[c] = __builtin_amdgcn_readlane(pend, 32) - a01;
+    vP[c] = half ? st1 - a01 : st0 - a00;                     // ring-relative read pointer
+    F0[c] = 0;                                                // words written to the ring
+    F1[c] = 0;
+    empty_err[c] = 0;
+    chunk_lane[c] = 2u * ((half ? a01 : a00) + lane2);       // byte offset of this lane's part
+    // the chunk held in registers is always the one starting at word F of the half
+    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, (half ? end1[c] : end0[c]) > 0u ? chunk_lane[c]
+                                                                                     : payload_bytes, 0, 0);
+    kfull = min(kfull, min(n0[c], n1[c]) >> 5);
+    kmax = max(kmax, max((n0[c] + 31u) >> 5, (n1[c] + 31u) >> 5));
+    g[c] = t * T.V + l;                                       // < 2^32: checked on the host
+    // rowb: byte offset of the row multiplier, g/2 or (slow rows) g of the row's pair
+    rowb[c] = slow_rows ? 4u : 0u;
+    col[c] = 0;
+    if (tile_ok[c]) {
+      const uint32_t row = g[c] / vpr;
+      col[c] = g[c] - row * vpr;
+      rowb[c] += 8u * row;
+    }
+  }
+  // A store past the end of the output per chain (dropped by the hardware): it
+  // makes the first round see the same queue of outstanding memory operations
+  // as every later round, so the compiler's waits stay exact.
+#pragma unroll
+  for (int c = 0; c < CH; ++c) __builtin_amdgcn_raw_buffer_store_b32(0u, rO, out_bytes, 0, 0);
 
   const uint32_t f0 = ((const EP_GLOBAL uint16_t*)T.freqs)[T.freq_base[0]];   // coset bit: frequency of c = 0
   uint32_t f0v = f0, f1v = M - f0;                          // per-lane copies for the selects
@@ -451,7 +494,6 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
   const uint32_t pw = T.f8z8 ? 0u : 1u;                     // width of the parity bit field
   const uint32_t sh8 = T.f8z8 ? 1u : 2u;
   const uint32_t empty = T.empty_mask;
-  const bool slow_rows = T.slow_rows != 0;
   const unsigned char* tbase = kGlobalEntries ? T.tab : lds;
   const uint32_t lut_bytes = uint32_t(lut_bytes_of(TL, B));
   // packed tables: fields 5..8 of b = 11 lie beyond the 16-bit LDS offset of
@@ -477,307 +519,398 @@ __device__ __forceinline__ void decode_pair(const DevTensor& T, uint32_t tile0, 
     m8d = int32_t(T.kvals[26]);
   }
 
-  // the chunk held in registers is always the one starting at word F of the half
-  u32x2 pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane, 0, 0);
-  // A store past the end of the output (dropped by the hardware): it makes the
-  // first round see the same queue of outstanding memory operations as every
-  // later round (chunk, then store), so the compiler's waits stay exact.
-  __builtin_amdgcn_raw_buffer_store_b32(0u, rO, out_bytes, 0, 0);
-
-  uint32_t g = t * T.V + l;                                 // < 2^32: checked on the host
-  // rowb: byte offset of the row multiplier, g/2 or (slow rows) g of the row's pair
-  uint32_t rowb = slow_rows ? 4u : 0u, col = 0;
-  if (tile_ok) {
-    const uint32_t row = g / vpr;
-    col = g - row * vpr;
-    rowb += 8u * row;
-  }
-
-  // One vector round.  In full rounds every lane of both halves has a vector,
-  // so the active-lane masks fold away.
-  auto round = [&](const uint32_t k, auto full) __attribute__((always_inline)) {
-    constexpr bool kFull = decltype(full)::value;
-    const bool active = kFull || (k * 32u + l) < n;
-    const uint32_t x_saved = x;
-    // Issued before the ring prefetch below: loads retire in order, so waiting
-    // for this one later does not also wait for the prefetch.
-    const float rv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, rowb, 0, 0));
-
-    P0 = __builtin_amdgcn_readlane(vP, 0);
-    P1 = __builtin_amdgcn_readlane(vP, 32);
-    // ---- ring: store the held chunk if it is useful and fits ...
+  // ---- ring staging of chain c before a segment of fields that reads at most
+  // `head` words per half: store the held chunk if it is useful and fits,
+  // catch up synchronously while the segment could read past the staged words
+  // (tile starts, dense runs), then fetch the chunk at the new fill position.
+  auto stage = [&](const int c, const uint32_t head) __attribute__((always_inline)) {
+    uint16_t* ring = rings + (2u * uint32_t(c) + half) * kRingWords;
+    const uint32_t P0 = __builtin_amdgcn_readlane(vP[c], 0);
+    const uint32_t P1 = __builtin_amdgcn_readlane(vP[c], 32);
     {
-      const bool w0 = F0 < end0 && F0 <= P0 + kRingSlack;
-      const bool w1 = F1 < end1 && F1 <= P1 + kRingSlack;
+      const bool w0 = F0[c] < end0[c] && F0[c] <= P0 + kRingSlack;
+      const bool w1 = F1[c] < end1[c] && F1[c] <= P1 + kRingSlack;
       // both halves' predicates as one lane mask (the branch takes it as exec);
       // the fill pointers packed in one scalar, a lane extracts its half's 16
       // bits (tile payloads stay below 2^16 words)
       if (__builtin_amdgcn_inverse_ballot_w64(half_mask(w0, w1))) {
-        const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
-        *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = pf;
+        const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
+        *reinterpret_cast<uint32_t*>(ring + ((F + lane2) & (kRingWords - 1u))) = pf[c];
       }
-      F0 += w0 ? kChunkWords : 0u;
-      F1 += w1 ? kChunkWords : 0u;
+      F0[c] += w0 ? kChunkWords : 0u;
+      F1[c] += w1 ? kChunkWords : 0u;
     }
-    // ... catch up synchronously if this round could read past the staged words
-    // (tile starts, and long runs above kChunkWords words per round) ...
     for (;;) {
-      const bool c0 = F0 < min(P0 + kRoundWords, end0);
-      const bool c1 = F1 < min(P1 + kRoundWords, end1);
+      const bool c0 = F0[c] < min(P0 + head, end0[c]);
+      const bool c1 = F1[c] < min(P1 + head, end1[c]);
       if (!(c0 || c1)) break;
       if (__builtin_amdgcn_inverse_ballot_w64(half_mask(c0, c1))) {
-        const uint32_t F = __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16);
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * F, 0, 0);
-        *reinterpret_cast<u32x2*>(ring + ((F & (kRingWords - 1u)) | lane4)) = v;
+        const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rP, chunk_lane[c] + 2u * F, 0, 0);
+        *reinterpret_cast<uint32_t*>(ring + ((F + lane2) & (kRingWords - 1u))) = v;
       }
-      F0 += c0 ? kChunkWords : 0u;
-      F1 += c1 ? kChunkWords : 0u;
+      F0[c] += c0 ? kChunkWords : 0u;
+      F1[c] += c1 ? kChunkWords : 0u;
     }
-    // ... and fetch the chunk at the new fill position for a later round.
-    pf = __builtin_amdgcn_raw_buffer_load_b64(rP, chunk_lane + 2u * __builtin_amdgcn_ubfe(F0 | (F1 << 16), hs, 16),
-                                              0, 0);
+    const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
+    const uint32_t E = half ? end1[c] : end0[c];
+    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, F < E ? chunk_lane[c] + 2u * F : payload_bytes, 0, 0);
+  };
 
-// Renormalisation: the lanes of a half whose state fell below 2^15 read the
-// next words of their tile in lane order.  A lane's word is its half's pointer
-// plus the number of reading lanes below it in the half (popcount of the
-// half's ballot bits under the lane).  Every lane reads (the index stays
-// inside the ring) and keeps the word only if it needed one: no exec masking
-// and no scalar pointer updates on the serial path.
-#define EP_RENORM()                                                                   \
-  {                                                                                   \
-    const bool rn = (x < kL) & active;                                                \
-    const uint32_t hm = uint32_t(__builtin_amdgcn_ballot_w64(rn) >> hs32);            \
-    const uint32_t idx = __builtin_popcount(__builtin_amdgcn_ubfe(hm, 0, l)) + vP;    \
-    uint32_t w = ring[idx & (kRingWords - 1u)];                                       \
-    asm volatile("" : "+v"(w)); /* keep the read unconditional */                    \
-    x = rn ? ((x << 16) | w) : x;                                                     \
-    vP += __builtin_popcount(hm);                                                     \
-  }
+  // Renormalisation of every chain: the lanes of a half whose state fell below
+  // 2^15 read the next words of their tile in lane order.  A lane's word is its
+  // half's pointer plus the number of reading lanes below it in the half
+  // (popcount of the half's ballot bits under the lane).  Every lane reads (the
+  // index stays inside the ring) and keeps the word only if it needed one: no
+  // exec masking and no scalar pointer updates on the serial path.  The chains
+  // go through each step together, so that their reads are in flight at the
+  // same time.
+  auto renorm = [&](const bool (&active)[CH]) __attribute__((always_inline)) {
+    bool rn[CH];
+    uint32_t hm[CH], w[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) rn[c] = (x[c] < kL) & active[c];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) hm[c] = uint32_t(__builtin_amdgcn_ballot_w64(rn[c]) >> hs32);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint16_t* ring = rings + (2u * uint32_t(c) + half) * kRingWords;
+      const uint32_t idx = __builtin_popcount(__builtin_amdgcn_ubfe(hm[c], 0, l)) + vP[c];
+      // a volatile read: it stays unconditional (not sunk into a branch on rn)
+      w[c] = *(const volatile EP_LDS uint16_t*)(ring + (idx & (kRingWords - 1u)));
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      x[c] = rn[c] ? ((x[c] << 16) | w[c]) : x[c];
+      vP[c] += __builtin_popcount(hm[c]);
+    }
+  };
+
+  // One vector round of every chain.  In full rounds every lane of every
+  // chain has a vector, so the active-lane masks fold away.
+  auto round = [&](const uint32_t k, auto full) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full)::value;
+    bool active[CH];
+    uint32_t x_saved[CH], cs[CH];
+    float vv[CH][9];
+    float rv[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      active[c] = kFull || (k * 32u + l) < n[c];
+      x_saved[c] = x[c];
+      // issued before the ring prefetch: loads retire in order, so waiting for
+      // the row multiplier later does not also wait for the prefetch
+      rv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, rowb[c], 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) stage(c, kHead0);
 
     // ---- field 0: coset bit (two-symbol table, resolved by one compare)
-    uint32_t q = x >> B;
-    uint32_t slot = x & MASK;
-    const bool c = slot >= f0v;
-    x = __umul24(c ? f1v : f0v, q) + slot - (c ? f0v : 0u);
-    EP_RENORM();
-    if (empty & 6u) empty_err |= __builtin_amdgcn_ballot_w64(active && ((empty >> (c ? 2 : 1)) & 1u));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t q = x[c] >> B;
+      const uint32_t slot = x[c] & MASK;
+      const bool cb = slot >= f0v;
+      cs[c] = cb ? 1u : 0u;
+      x[c] = __umul24(cb ? f1v : f0v, q) + slot - (cb ? f0v : 0u);
+    }
+    renorm(active);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (empty & 6u) empty_err[c] |= __builtin_amdgcn_ballot_w64(active[c] && ((empty >> (cs[c] ? 2 : 1)) & 1u));
 
-    // ---- fields z1..z7, m; vv[f] becomes 2 z_f + c (exact in fp32)
-    float vv[9];
-    uint32_t par;
-    if (is_packed(TL)) {
-      uint32_t ev[9];
-      uint32_t lbl = c ? (M << 2) : 0u;                  // byte offset of the coset's table
-      uint32_t lbh = lbl + (kSplit ? (8u << B) * 4u : 0u);
-      // opaque to the optimiser, so that the lookup address stays one
-      // v_and_or_b32 with the table offset folded into the LDS instruction
-      asm volatile("" : "+v"(lbl), "+v"(lbh));
+    // ---- fields z1..z7, m; vv[c][f] becomes 2 z_f + c (exact in fp32)
+    uint32_t par[CH];
+    if constexpr (is_packed(TL)) {
+      uint32_t ev[CH][9], lbl[CH], lbh[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        lbl[c] = cs[c] ? (M << 2) : 0u;                    // byte offset of the coset's table
+        lbh[c] = lbl[c] + (kSplit ? (8u << B) * 4u : 0u);
+        // opaque to the optimiser, so that the lookup address stays one
+        // v_and_or_b32 with the table offset folded into the LDS instruction
+        asm volatile("" : "+v"(lbl[c]), "+v"(lbh[c]));
+      }
 #pragma unroll
       for (int f = 1; f <= 8; ++f) {
         const bool hi = kSplit && f >= 5;
         const uint32_t toff = (uint32_t(2 * (f - 1) - (hi ? 8 : 0)) << B) * 4u;
-        const uint32_t e = *reinterpret_cast<const uint32_t*>(lds + (((x << 2) & (MASK << 2)) | (hi ? lbh : lbl)) + toff);
-        q = x >> B;
-        x = __umul24(__builtin_amdgcn_ubfe(e, 11, fw), q) + (e & 0x7FFu);
-        ev[f] = e;
-        EP_RENORM();
-      }
-      if (kDirectable && direct) {
-        // direct entries: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 +
-        // (2 z + c - 2 dmin), and one constant per field (the same for both
-        // cosets) turns it into 2 z + c.  Bit 23 of an entry is the parity of
-        // z - dmin, so the XOR of z1..z7's entries gives the parity of their
-        // sum up to the parity of the minima, which the field-8 constant and
-        // multiplier absorb: 2 z8 + c = (4 (m - dmin8) + c) + 2 par + 4 dmin8.
+        uint32_t e[CH];
 #pragma unroll
-        for (int f = 1; f <= 7; ++f)
-          vv[f] = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22)) + kd[f - 1];
-        const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
-            __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
-            __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96), ev[7], 0x96);
-        par = __builtin_amdgcn_ubfe(x3, 23, pw);
-        const int32_t u8 = __mul24(int32_t(par), m8d) + int32_t(__builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[8], 22));
-        vv[8] = __builtin_bit_cast(float, u8) + k8d;
-      } else {
-      // value of z_f.  Packed: 0x4B400000 | (e >> 22) is the float
-      // 2^23 + 2^22 + 2 s (+1 when f = 2^11), and the per-table constant turns
-      // it into 2 z + c.  Wide: the same bits give 2^23 + 2^22 + s, the
-      // constant turns it into z, and an exact fma makes 2 z + c.
-      const int kaddr = c ? 4 : 0;
-      const float cf = c ? 1.0f : 0.0f;
+        for (int c = 0; c < CH; ++c)
+          e[c] = *reinterpret_cast<const uint32_t*>(lds + (((x[c] << 2) & (MASK << 2)) | (hi ? lbh[c] : lbl[c])) +
+                                                    toff);
 #pragma unroll
-      for (int f = 1; f <= 7; ++f) {
-        const float u = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[f], 22));
-        const float kf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 8 * (f - 1), int(kreg)));
-        vv[f] = kWide ? __builtin_fmaf(u - kf, 2.0f, cf) : u - kf;
+        for (int c = 0; c < CH; ++c) {
+          const uint32_t q = x[c] >> B;
+          x[c] = __umul24(__builtin_amdgcn_ubfe(e[c], 11, fw), q) + (e[c] & 0x7FFu);
+          ev[c][f] = e[c];
+        }
+        if (f == 5) {
+          // the words fields 5..8 can read must be staged (rarely not yet)
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const uint32_t P0 = __builtin_amdgcn_readlane(vP[c], 0);
+            const uint32_t P1 = __builtin_amdgcn_readlane(vP[c], 32);
+            if (F0[c] < min(P0 + kHead1, end0[c]) || F1[c] < min(P1 + kHead1, end1[c]))
+              stage(c, kHead1);
+          }
+        }
+        renorm(active);
       }
-      // parity of z1 + ... + z7: bit kSymShift of each entry is the parity of
-      // its symbol index, the constant supplies the parity of the minima
-      const uint32_t kp = uint32_t(__builtin_amdgcn_ds_bpermute(kaddr + 64, int(kreg)));
-      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
-          __builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
-          __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
-          ev[7] ^ kp, 0x96);
-      par = __builtin_amdgcn_ubfe(x3, kSymShift, pw);
-      // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + (c + 4 min), the
-      // parenthesis being part of the per-table constant (a directly coded
-      // z8: 2 s8 + (c + 2 min), with the parity field of width 0)
-      const uint32_t u8 = ((ev[8] >> kSymShift) << sh8) + ((par << 1) | 0x4B400000u);
-      const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
-      vv[8] = __builtin_bit_cast(float, u8) - k8;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        if (kDirectable && direct) {
+          // direct entries: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 +
+          // (2 z + c - 2 dmin), and one constant per field (the same for both
+          // cosets) turns it into 2 z + c.  Bit 23 of an entry is the parity of
+          // z - dmin, so the XOR of z1..z7's entries gives the parity of their
+          // sum up to the parity of the minima, which the field-8 constant and
+          // multiplier absorb: 2 z8 + c = (4 (m - dmin8) + c) + 2 par + 4 dmin8.
+#pragma unroll
+          for (int f = 1; f <= 7; ++f)
+            vv[c][f] = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[c][f], 22)) +
+                       kd[f - 1];
+          const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+              __builtin_amdgcn_bitop3_b32(ev[c][1], ev[c][2], ev[c][3], 0x96),
+              __builtin_amdgcn_bitop3_b32(ev[c][4], ev[c][5], ev[c][6], 0x96), ev[c][7], 0x96);
+          par[c] = __builtin_amdgcn_ubfe(x3, 23, pw);
+          const int32_t u8 = __mul24(int32_t(par[c]), m8d) +
+                             int32_t(__builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[c][8], 22));
+          vv[c][8] = __builtin_bit_cast(float, u8) + k8d;
+        } else {
+          // value of z_f.  Packed: 0x4B400000 | (e >> 22) is the float
+          // 2^23 + 2^22 + 2 s (+1 when f = 2^11), and the per-table constant turns
+          // it into 2 z + c.  Wide: the same bits give 2^23 + 2^22 + s, the
+          // constant turns it into z, and an exact fma makes 2 z + c.
+          const int kaddr = cs[c] ? 4 : 0;
+          const float cf = cs[c] ? 1.0f : 0.0f;
+#pragma unroll
+          for (int f = 1; f <= 7; ++f) {
+            const float u = __builtin_bit_cast(float, __builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[c][f], 22));
+            const float kf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 8 * (f - 1), int(kreg)));
+            vv[c][f] = kWide ? __builtin_fmaf(u - kf, 2.0f, cf) : u - kf;
+          }
+          // parity of z1 + ... + z7: bit kSymShift of each entry is the parity of
+          // its symbol index, the constant supplies the parity of the minima
+          const uint32_t kp = uint32_t(__builtin_amdgcn_ds_bpermute(kaddr + 64, int(kreg)));
+          const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+              __builtin_amdgcn_bitop3_b32(ev[c][1], ev[c][2], ev[c][3], 0x96),
+              __builtin_amdgcn_bitop3_b32(ev[c][4], ev[c][5], ev[c][6], 0x96), ev[c][7] ^ kp, 0x96);
+          par[c] = __builtin_amdgcn_ubfe(x3, kSymShift, pw);
+          // z8 = 2 m + parity: 2 z8 + c = 4 s8 + 2 par + (c + 4 min), the
+          // parenthesis being part of the per-table constant (a directly coded
+          // z8: 2 s8 + (c + 2 min), with the parity field of width 0)
+          const uint32_t u8 = ((ev[c][8] >> kSymShift) << sh8) + ((par[c] << 1) | 0x4B400000u);
+          const float k8 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(kaddr + 56, int(kreg)));
+          vv[c][8] = __builtin_bit_cast(float, u8) - k8;
+        }
       }
     } else if constexpr (SP) {
       // per-slot entries f | (slot - cum) << 7 | parity << 15 and the slot
       // symbol's value 2 z + c (i16), both in LDS (b = 11: 64 KB each)
       static_assert(BT == 11, "per-slot entries are built for b = 11");
-      uint32_t ev[9];
-      uint32_t lbl = c ? (M << 1) : 0u;                  // byte offset of the coset's map
-      asm volatile("" : "+v"(lbl));
+      uint32_t ev[CH][9], lbl[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        lbl[c] = cs[c] ? (M << 1) : 0u;                    // byte offset of the coset's map
+        asm volatile("" : "+v"(lbl[c]));
+      }
 #pragma unroll
       for (int f = 1; f <= 8; ++f) {
         const uint32_t toff = (uint32_t(2 * (f - 1)) << B) * 2u;       // at most 57344
-        const uint32_t a = ((x << 1) & (MASK << 1)) | lbl;
-        const uint32_t e = *reinterpret_cast<const uint16_t*>(lds + a + toff);
-        // the values follow the 16 entry maps (64 KB): a second base register
-        const uint32_t av = a | (uint32_t(16) << (B + 1));
-        vv[f] = float(*reinterpret_cast<const int16_t*>(lds + av + toff));
-        q = x >> B;
-        x = __umul24(e & 0x7Fu, q) + __builtin_amdgcn_ubfe(e, 7, 7);
-        ev[f] = e;
-        EP_RENORM();
+        uint32_t e[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const uint32_t a = ((x[c] << 1) & (MASK << 1)) | lbl[c];
+          e[c] = *reinterpret_cast<const uint16_t*>(lds + a + toff);
+          // the values follow the 16 entry maps (64 KB): a second base register
+          const uint32_t av = a | (uint32_t(16) << (B + 1));
+          vv[c][f] = float(*reinterpret_cast<const int16_t*>(lds + av + toff));
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const uint32_t q = x[c] >> B;
+          x[c] = __umul24(e[c] & 0x7Fu, q) + __builtin_amdgcn_ubfe(e[c], 7, 7);
+          ev[c][f] = e[c];
+        }
+        if (f == 5) {
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const uint32_t P0 = __builtin_amdgcn_readlane(vP[c], 0);
+            const uint32_t P1 = __builtin_amdgcn_readlane(vP[c], 32);
+            if (F0[c] < min(P0 + kHead1, end0[c]) || F1[c] < min(P1 + kHead1, end1[c]))
+              stage(c, kHead1);
+          }
+        }
+        renorm(active);
       }
-      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(ev[1], ev[2], ev[3], 0x96),
-                                                      __builtin_amdgcn_bitop3_b32(ev[4], ev[5], ev[6], 0x96),
-                                                      ev[7], 0x96);
-      par = __builtin_amdgcn_ubfe(x3, 15, pw);
-      vv[8] = vv[8] + float(par << 1);                   // the m values are 4 m + c (z8: 2 z8 + c)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+            __builtin_amdgcn_bitop3_b32(ev[c][1], ev[c][2], ev[c][3], 0x96),
+            __builtin_amdgcn_bitop3_b32(ev[c][4], ev[c][5], ev[c][6], 0x96), ev[c][7], 0x96);
+        par[c] = __builtin_amdgcn_ubfe(x3, 15, pw);
+        vv[c][8] = vv[c][8] + float(par[c] << 1);           // the m values are 4 m + c (z8: 2 z8 + c)
+      }
     } else {
-      uint32_t sv[9];
-      const uint32_t lb = c ? M : 0u;                    // coset offset inside each table pair
-      // symbol tables: coset base including the block's own offset, so that
-      // the per-field LDS offsets fit the 16-bit immediate
-      uint32_t cb = c ? lut_bytes + S * 4u : lut_bytes;
-      if (TL == kTabNarrow) asm volatile("" : "+v"(cb));
+      uint32_t sv[CH][9], lb[CH], cb[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        lb[c] = cs[c] ? M : 0u;                            // coset offset inside each table pair
+        // symbol tables: coset base including the block's own offset, so that
+        // the per-field LDS offsets fit the 16-bit immediate
+        cb[c] = cs[c] ? lut_bytes + S * 4u : lut_bytes;
+        if (TL == kTabNarrow) asm volatile("" : "+v"(cb[c]));
+      }
 #pragma unroll
       for (int f = 1; f <= 8; ++f) {
-        const uint32_t addr = (x & MASK) | lb;           // slot + coset * 2^b
-        uint32_t s;
-        if (kWs) s = reinterpret_cast<const uint16_t*>(tbase)[(uint32_t(2 * (f - 1)) << B) + addr];
-        else if (kHyb) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr];
-        else s = lds[(uint32_t(2 * (f - 1)) << B) + addr];
-        const uint32_t eo = cb + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
-        const uint32_t e = *reinterpret_cast<const uint32_t*>(tbase + eo);
-        vv[f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
-        q = x >> B;
-        x = __umul24(e & (kGlobalEntries ? 0xFFFFu : 0x7FFFu), q) + (addr - (e >> 16));
-        sv[f] = kGlobalEntries ? s : e;
-        EP_RENORM();
+        uint32_t e[CH], addr[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          addr[c] = (x[c] & MASK) | lb[c];                 // slot + coset * 2^b
+          uint32_t s;
+          if (kWs) s = reinterpret_cast<const uint16_t*>(tbase)[(uint32_t(2 * (f - 1)) << B) + addr[c]];
+          else if (kHyb) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr[c]];
+          else s = lds[(uint32_t(2 * (f - 1)) << B) + addr[c]];
+          const uint32_t eo = cb[c] + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
+          e[c] = *reinterpret_cast<const uint32_t*>(tbase + eo);
+          vv[c][f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
+          sv[c][f] = kGlobalEntries ? s : e[c];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const uint32_t q = x[c] >> B;
+          x[c] = __umul24(e[c] & (kGlobalEntries ? 0xFFFFu : 0x7FFFu), q) + (addr[c] - (e[c] >> 16));
+        }
+        if (f == 5) {
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const uint32_t P0 = __builtin_amdgcn_readlane(vP[c], 0);
+            const uint32_t P1 = __builtin_amdgcn_readlane(vP[c], 32);
+            if (F0[c] < min(P0 + kHead1, end0[c]) || F1[c] < min(P1 + kHead1, end1[c]))
+              stage(c, kHead1);
+          }
+        }
+        renorm(active);
       }
-      const uint32_t x3 = __builtin_amdgcn_bitop3_b32(__builtin_amdgcn_bitop3_b32(sv[1], sv[2], sv[3], 0x96),
-                                                      __builtin_amdgcn_bitop3_b32(sv[4], sv[5], sv[6], 0x96),
-                                                      sv[7], 0x96);
-      // narrow: bit 15 of the symbol entries is the parity of z; workspace:
-      // parity of the symbol indices, corrected by the parity of the minima
-      par = TL == kTabNarrow ? __builtin_amdgcn_ubfe(x3, 15, pw) : (x3 ^ (kpar >> (c ? 1 : 0))) & pw;
-      vv[8] = vv[8] + float(par << 1);                   // the m table holds 4 m + c (z8: 2 z8 + c)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+            __builtin_amdgcn_bitop3_b32(sv[c][1], sv[c][2], sv[c][3], 0x96),
+            __builtin_amdgcn_bitop3_b32(sv[c][4], sv[c][5], sv[c][6], 0x96), sv[c][7], 0x96);
+        // narrow: bit 15 of the symbol entries is the parity of z; workspace:
+        // parity of the symbol indices, corrected by the parity of the minima
+        par[c] = TL == kTabNarrow ? __builtin_amdgcn_ubfe(x3, 15, pw) : (x3 ^ (kpar >> (cs[c] ? 1 : 0))) & pw;
+        vv[c][8] = vv[c][8] + float(par[c] << 1);           // the m table holds 4 m + c (z8: 2 z8 + c)
+      }
     }
-#undef EP_RENORM
-    x = active ? x : x_saved;
 
     // ---- y = (z + c/2) * g, computed as (2 z + c) * (g/2) when g/2 is exact
     // (the row multiplier array then holds g/2; otherwise g and the slow form)
-    const uint32_t ob = active ? (g + k * 32u) * out_vec_bytes(OK) : out_bytes;
-    if (OK == kOutLattice) {
-      const i32x4 lo4 = {int(vv[1]), int(vv[2]), int(vv[3]), int(vv[4])};
-      const i32x4 hi4 = {int(vv[5]), int(vv[6]), int(vv[7]), int(vv[8])};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo4), rO, ob, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi4), rO, ob + 16u, 0, 0);
-    } else {
-      // slow rows: rv is g and 2 z + c is halved first (exactly)
-      if (slow_rows) {
 #pragma unroll
-        for (int i = 1; i <= 8; ++i) vv[i] = __fmul_rn(vv[i], 0.5f);
-      }
-      float y[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(vv[i + 1], rv);
-      if (OK == kOutBF16) {
-        const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                         pack_bf16x2(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
-      } else if (OK == kOutFP16) {
-        const u32x4 w = {pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
-                         pack_f16x2(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
-      } else if (OK == kOutFP32) {
-        const u32x4 lo = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
-        const u32x4 hi = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]), __float_as_uint(y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(lo, rO, ob, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(hi, rO, ob + 16u, 0, 0);
-      } else if (OK == kOutFP8) {
-        const u32x2 w = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
+    for (int c = 0; c < CH; ++c) {
+      x[c] = active[c] ? x[c] : x_saved[c];
+      const uint32_t ob = active[c] ? (g[c] + k * 32u) * out_vec_bytes(OK) : out_bytes;
+      float* v = vv[c];
+      if (OK == kOutLattice) {
+        const i32x4 lo4 = {int(v[1]), int(v[2]), int(v[3]), int(v[4])};
+        const i32x4 hi4 = {int(v[5]), int(v[6]), int(v[7]), int(v[8])};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo4), rO, ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi4), rO, ob + 16u, 0, 0);
       } else {
-        // INT8 codes; UINT8 adds the offset 128
-        const u32x2 w = {int8_codes4<OK == kOutUINT8>(y[0], y[1], y[2], y[3]),
-                         int8_codes4<OK == kOutUINT8>(y[4], y[5], y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
+        // slow rows: rv is g and 2 z + c is halved first (exactly)
+        if (slow_rows) {
+#pragma unroll
+          for (int i = 1; i <= 8; ++i) v[i] = __fmul_rn(v[i], 0.5f);
+        }
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(v[i + 1], rv[c]);
+        if (OK == kOutBF16) {
+          const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                           pack_bf16x2(y[6], y[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
+        } else if (OK == kOutFP16) {
+          const u32x4 w = {pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]), pack_f16x2(y[4], y[5]),
+                           pack_f16x2(y[6], y[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rO, ob, 0, 0);
+        } else if (OK == kOutFP32) {
+          const u32x4 lo = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                            __float_as_uint(y[3])};
+          const u32x4 hi = {__float_as_uint(y[4]), __float_as_uint(y[5]), __float_as_uint(y[6]),
+                            __float_as_uint(y[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(lo, rO, ob, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(hi, rO, ob + 16u, 0, 0);
+        } else if (OK == kOutFP8) {
+          const u32x2 w = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
+          __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
+        } else {
+          // INT8 codes; UINT8 adds the offset 128
+          const u32x2 w = {int8_codes4<OK == kOutUINT8>(y[0], y[1], y[2], y[3]),
+                           int8_codes4<OK == kOutUINT8>(y[4], y[5], y[6], y[7])};
+          __builtin_amdgcn_raw_buffer_store_b64(w, rO, ob, 0, 0);
+        }
       }
-    }
-    col += 32u;
-    if (col >= vpr) {                       // rows of at least 32 vectors wrap at most once
-      col -= vpr;
-      rowb += 8u;
-      while (col >= vpr) {
-        col -= vpr;
-        rowb += 8u;
+      col[c] += 32u;
+      if (col[c] >= vpr) {                  // rows of at least 32 vectors wrap at most once
+        col[c] -= vpr;
+        rowb[c] += 8u;
+        while (col[c] >= vpr) {
+          col[c] -= vpr;
+          rowb[c] += 8u;
+        }
       }
     }
   };
-  const uint32_t kfull = min(n0, n1) >> 5;
   uint32_t k = 0;
   for (; k < kfull; ++k) round(k, std::true_type{});
   for (; k < kmax; ++k) round(k, std::false_type{});
 
   // ---- end-of-tile invariants: every state back at 2^15, every word consumed
-  const uint64_t bad_state = __builtin_amdgcn_ballot_w64(x != kL);
-  const uint64_t bad_len_m = __builtin_amdgcn_ballot_w64(bad_len);
-  if (tile_ok && l == 0 && T.status) {
-    const uint32_t Pm = vP, Em = half ? end1 : end0;
-    const uint32_t sh = half ? 32u : 0u;
-    int st = EP_TILE_OK;
-    if (uint32_t(bad_len_m >> sh)) st = EP_TILE_BAD_LENGTH;
-    else if (Pm > Em) st = EP_TILE_OVERRUN;
-    else if (uint32_t(empty_err >> sh)) st = EP_TILE_EMPTY_TABLE;
-    else if (uint32_t(bad_state >> sh)) st = EP_TILE_BAD_STATE;
-    else if (Pm != Em) st = EP_TILE_BAD_LENGTH;
-    ((EP_GLOBAL int32_t*)T.status)[t] = st;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint64_t bad_state = __builtin_amdgcn_ballot_w64(x[c] != kL);
+    const uint64_t bad_len_m = __builtin_amdgcn_ballot_w64(bad_len[c]);
+    if (tile_ok[c] && l == 0 && T.status) {
+      const uint32_t Pm = vP[c], Em = half ? end1[c] : end0[c];
+      const uint32_t sh = half ? 32u : 0u;
+      int st = EP_TILE_OK;
+      if (uint32_t(bad_len_m >> sh)) st = EP_TILE_BAD_LENGTH;
+      else if (Pm > Em) st = EP_TILE_OVERRUN;
+      else if (uint32_t(empty_err[c] >> sh)) st = EP_TILE_EMPTY_TABLE;
+      else if (uint32_t(bad_state >> sh)) st = EP_TILE_BAD_STATE;
+      else if (Pm != Em) st = EP_TILE_BAD_LENGTH;
+      ((EP_GLOBAL int32_t*)T.status)[tile0 + 2u * uint32_t(c) + half] = st;
+    }
   }
 }
 
 // Persistent decode kernel.  Block i owns a contiguous range of chunks (up to
 // tiles_per_chunk tiles of one tensor each), which splits into runs of chunks
 // from the same tensor.  For each run the block stages the tensor's decode
-// tables (LDS layouts); then each wave takes pairs of consecutive tiles (one
-// per half-wave) from a counter until the run is exhausted.  Taking work
-// dynamically keeps all of a block's waves busy to the end: the SIMD's issue
-// arbitration favours older waves, so equal static shares finish at very
-// different times.  The counter of a run is the word of `ctr` at the run's
-// first chunk (LDS is fully used by the tables and rings); a wave claims its
-// next pair before decoding the current one, so the atomic's latency is hidden.
-template <int BT, int TL, int OK>
+// tables (LDS layouts); then each wave takes groups of 2 * CH consecutive tiles
+// (CH chains of one tile per half-wave) from a counter until the run is
+// exhausted.  Taking work dynamically keeps all of a block's waves busy to the
+// end: the SIMD's issue arbitration favours older waves, so equal static shares
+// finish at very different times.  The counter of a run is the word of `ctr`
+// at the run's first chunk (LDS is fully used by the tables and rings); a wave
+// claims its next group before decoding the current one, so the atomic's
+// latency is hidden.
+template <int BT, int TL, int OK, int CH>
 __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restrict__ tens,
                                                         const Chunk* __restrict__ chunks,
                                                         uint32_t* __restrict__ ctr,
                                                         uint32_t nchunks, uint32_t tiles_per_chunk) {
   constexpr size_t kTab = lds_table_bytes_of(TL, BT);
-  __shared__ __align__(16) unsigned char smem[kTab + kRingBytes];
+  constexpr uint32_t kGroup = 2u * CH;                     // tiles per wave group
+  __shared__ __align__(16) unsigned char smem[kTab + ring_bytes_of(CH)];
   const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
   const uint32_t c0 = blockIdx.x * per;
   const uint32_t c1 = min(nchunks, c0 + per);
   const bool lane0 = (threadIdx.x & 63u) == 0;
-  // LDS: [decode tables (LDS layouts)][32 rings of kRingWords]
-  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 5) * kRingWords;
+  // LDS: [decode tables (LDS layouts)][2 * CH rings of kRingWords per wave]
+  uint16_t* rings = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 6) * (kGroup * kRingWords);
   for (uint32_t ci = c0; ci < c1;) {
     const Chunk ch = chunks[ci];
     const DevTensor& T = tens[ch.tensor];
@@ -785,7 +918,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     const uint32_t left = (T.T - ch.tile0 + tiles_per_chunk - 1) / tiles_per_chunk;
     const uint32_t cn = min(c1, ci + left);
     const uint32_t t_end = min(T.T, ch.tile0 + (cn - ci) * tiles_per_chunk);
-    const uint32_t npairs = (t_end - ch.tile0 + 1) / 2;
+    const uint32_t ngroups = (t_end - ch.tile0 + kGroup - 1) / kGroup;
     __syncthreads();                       // every wave is done with the previous run
     if (threadIdx.x == 0) __hip_atomic_store(ctr + ci, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // hybrid layout: the per-slot entry maps when the build kept them, else the slot maps
@@ -797,18 +930,18 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = src[i];
     }
     __syncthreads();
-    // the first pair of each wave is its own index, which spreads a short run
-    // over the SIMDs (wave w runs on SIMD w mod 4); later pairs come from the counter
-    uint32_t pr = threadIdx.x >> 6, nx = 0;
-    while (pr < npairs) {
+    // the first group of each wave is its own index, which spreads a short run
+    // over the SIMDs (wave w runs on SIMD w mod 4); later groups come from the counter
+    uint32_t gr = threadIdx.x >> 6, nx = 0;
+    while (gr < ngroups) {
       if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
       if constexpr (has_split(TL, BT)) {
-        if (split) decode_pair<BT, TL, OK, true>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
-        else decode_pair<BT, TL, OK, false>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+        if (split) decode_tiles<BT, TL, OK, true, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else decode_tiles<BT, TL, OK, false, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       } else {
-        decode_pair<BT, TL, OK, false>(T, ch.tile0 + 2u * pr, t_end, smem, ring);
+        decode_tiles<BT, TL, OK, false, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       }
-      pr = __builtin_amdgcn_readfirstlane(nx);
+      gr = __builtin_amdgcn_readfirstlane(nx);
     }
     ci = cn;
   }
@@ -840,15 +973,15 @@ uint32_t choose_variant(const ep_tensor_desc& d) {
   for (int k = 1; k < kTables; ++k) amax = std::max(amax, d.alphabet[k]);
   bool single = false;                                 // a one-symbol table (f = 2^b)
   for (int k = 1; k < kTables; ++k) single |= d.alphabet[k] == 1;
-  if (d.prob_bits <= 11 && amax <= 512 && table_bytes_of(kTabPacked, d.prob_bits) + kRingBytes <= kMaxLds)
+  if (d.prob_bits <= 11 && amax <= 512 && table_bytes_of(kTabPacked, d.prob_bits) + kRingBytesMax <= kMaxLds)
     return kVarP9 + (d.prob_bits - 9);
   // the wide entry holds f in 11 bits: every f < 2^11 (no one-symbol table at b = 11)
   if ((d.prob_bits == 10 || d.prob_bits == 11) && amax <= 1024 && !(d.prob_bits == 11 && single) &&
-      table_bytes_of(kTabPackedWide, d.prob_bits) + kRingBytes <= kMaxLds)
+      table_bytes_of(kTabPackedWide, d.prob_bits) + kRingBytesMax <= kMaxLds)
     return kVarW10 + (d.prob_bits - 10);
-  if (d.prob_bits == 12 && amax <= 256 && table_bytes_of(kTabNarrow, 12) + kRingBytes <= kMaxLds)
+  if (d.prob_bits == 12 && amax <= 256 && table_bytes_of(kTabNarrow, 12) + kRingBytesMax <= kMaxLds)
     return kVarN12;
-  if ((d.prob_bits == 11 || d.prob_bits == 12) && lds_table_bytes_of(kTabHybrid, d.prob_bits) + kRingBytes <= kMaxLds)
+  if ((d.prob_bits == 11 || d.prob_bits == 12) && lds_table_bytes_of(kTabHybrid, d.prob_bits) + kRingBytesMax <= kMaxLds)
     return kVarH11 + (d.prob_bits - 11);
   return kVarWs;
 }
@@ -951,7 +1084,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
 }
 
 struct Group {
-  uint32_t chunk_begin, nchunks, grid, tiles_per_chunk;
+  uint32_t chunk_begin, nchunks, grid, tiles_per_chunk, chains;
 };
 
 struct PlanImpl {
@@ -962,40 +1095,45 @@ struct PlanImpl {
   Group groups[kNumGroups];
 };
 static_assert(sizeof(PlanImpl) <= sizeof(ep_batch_plan), "plan record too large");
-constexpr uint64_t kPlanMagic = 0x45504c414e763036ull;
+constexpr uint64_t kPlanMagic = 0x45504c414e763037ull;
 
 using KernelFn = void (*)(const DevTensor*, const Chunk*, uint32_t*, uint32_t, uint32_t);
 
-template <int BT, int TL>
+template <int BT, int TL, int CH>
 KernelFn kernel_for_kind(int ok) {
   switch (ok) {
-    case kOutBF16: return decode_kernel<BT, TL, kOutBF16>;
-    case kOutFP8: return decode_kernel<BT, TL, kOutFP8>;
-    case kOutINT8: return decode_kernel<BT, TL, kOutINT8>;
-    case kOutFP16: return decode_kernel<BT, TL, kOutFP16>;
-    case kOutFP32: return decode_kernel<BT, TL, kOutFP32>;
-    case kOutUINT8: return decode_kernel<BT, TL, kOutUINT8>;
-    default: return decode_kernel<BT, TL, kOutLattice>;
+    case kOutBF16: return decode_kernel<BT, TL, kOutBF16, CH>;
+    case kOutFP8: return decode_kernel<BT, TL, kOutFP8, CH>;
+    case kOutINT8: return decode_kernel<BT, TL, kOutINT8, CH>;
+    case kOutFP16: return decode_kernel<BT, TL, kOutFP16, CH>;
+    case kOutFP32: return decode_kernel<BT, TL, kOutFP32, CH>;
+    case kOutUINT8: return decode_kernel<BT, TL, kOutUINT8, CH>;
+    default: return decode_kernel<BT, TL, kOutLattice, CH>;
   }
 }
 
-KernelFn kernel_of(uint32_t group) {
+template <int CH>
+KernelFn kernel_of_chains(uint32_t group) {
   const int ok = int(group % kNumOutKinds);
   switch (group / kNumOutKinds) {
-    case kVarP9: return kernel_for_kind<9, kTabPacked>(ok);
-    case kVarP10: return kernel_for_kind<10, kTabPacked>(ok);
-    case kVarP11: return kernel_for_kind<11, kTabPacked>(ok);
-    case kVarW10: return kernel_for_kind<10, kTabPackedWide>(ok);
-    case kVarW11: return kernel_for_kind<11, kTabPackedWide>(ok);
-    case kVarN12: return kernel_for_kind<12, kTabNarrow>(ok);
-    case kVarH11: return kernel_for_kind<11, kTabHybrid>(ok);
-    case kVarH12: return kernel_for_kind<12, kTabHybrid>(ok);
-    default: return kernel_for_kind<0, kTabWorkspace>(ok);
+    case kVarP9: return kernel_for_kind<9, kTabPacked, CH>(ok);
+    case kVarP10: return kernel_for_kind<10, kTabPacked, CH>(ok);
+    case kVarP11: return kernel_for_kind<11, kTabPacked, CH>(ok);
+    case kVarW10: return kernel_for_kind<10, kTabPackedWide, CH>(ok);
+    case kVarW11: return kernel_for_kind<11, kTabPackedWide, CH>(ok);
+    case kVarN12: return kernel_for_kind<12, kTabNarrow, CH>(ok);
+    case kVarH11: return kernel_for_kind<11, kTabHybrid, CH>(ok);
+    case kVarH12: return kernel_for_kind<12, kTabHybrid, CH>(ok);
+    default: return kernel_for_kind<0, kTabWorkspace, CH>(ok);
   }
+}
+
+KernelFn kernel_of(uint32_t group, uint32_t chains) {
+  return chains == 2 ? kernel_of_chains<2>(group) : kernel_of_chains<1>(group);
 }
 
 // Persistent grid: as many blocks as can be resident at once (at least one).
-int resident_grid(uint32_t group, uint32_t* grid) {
+int resident_grid(uint32_t group, uint32_t chains, uint32_t* grid) {
   static int cus = 0;
   hipError_t e;
   if (cus == 0) {
@@ -1005,7 +1143,7 @@ int resident_grid(uint32_t group, uint32_t* grid) {
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("device query: ") + hipGetErrorString(e));
   }
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_of(group)),
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel_of(group, chains)),
                                                    kBlock, 0);
   if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
   const uint64_t g = uint64_t(std::max(per_cu, 1)) * uint64_t(std::max(cus, 1));
@@ -1013,14 +1151,23 @@ int resident_grid(uint32_t group, uint32_t* grid) {
   return EP_OK;
 }
 
-// Tiles per chunk: full blocks (kTilesPerChunk) when there is enough work to
-// fill every resident block many times over; otherwise spread the tiles over
-// all resident blocks (even counts, one tile per half-wave), since a tile is a
-// sequential unit and a small batch is bound by the per-tile decode latency.
-uint32_t tiles_per_chunk(size_t tiles, uint32_t resident) {
-  if (tiles >= size_t(kTilesPerChunk) * resident) return kTilesPerChunk;
+// Chains per wave: two tile pairs decoded together hide more of the per-symbol
+// latency, but need four tiles per wave; a batch too small to give every
+// resident wave several groups of four runs one pair per wave.
+uint32_t chains_for(size_t tiles, uint32_t resident) {
+  return tiles >= size_t(4) * 2 * kMaxChains * kWavesPerBlock * resident ? 2u : 1u;
+}
+
+// Tiles per chunk: full blocks (2 * chains tiles per wave) when there is enough
+// work to fill every resident block many times over; otherwise spread the
+// tiles over all resident blocks (even counts, one tile per half-wave), since a
+// tile is a sequential unit and a small batch is bound by the per-tile decode
+// latency.
+uint32_t tiles_per_chunk(size_t tiles, uint32_t resident, uint32_t chains) {
+  const uint32_t full = 2u * chains * kWavesPerBlock;
+  if (tiles >= size_t(full) * resident) return full;
   const size_t per = (tiles + 2 * size_t(resident) - 1) / (2 * size_t(resident));
-  return uint32_t(std::min<size_t>(kTilesPerChunk, std::max<size_t>(2, 2 * per)));
+  return uint32_t(std::min<size_t>(full, std::max<size_t>(2, 2 * per)));
 }
 
 }  // namespace
@@ -1082,12 +1229,18 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   for (uint32_t v = 0; v < kNumGroups; ++v) {
     Group& G = P->groups[v];
     G.grid = 0;
-    G.tiles_per_chunk = kTilesPerChunk;
+    G.chains = 1;
+    G.tiles_per_chunk = 2u * kWavesPerBlock;
     if (L.group_tiles[v] == 0) continue;
     uint32_t resident = 0;
-    rc = resident_grid(v, &resident);
+    rc = resident_grid(v, kMaxChains, &resident);
     if (rc != EP_OK) return rc;
-    G.tiles_per_chunk = tiles_per_chunk(L.group_tiles[v], resident);
+    G.chains = chains_for(L.group_tiles[v], resident);
+    if (G.chains != kMaxChains) {
+      rc = resident_grid(v, G.chains, &resident);
+      if (rc != EP_OK) return rc;
+    }
+    G.tiles_per_chunk = tiles_per_chunk(L.group_tiles[v], resident, G.chains);
     for (int i = 0; i < n; ++i)
       if (L.group[i] == v) group_chunks[v] += (descs[i].num_tiles + G.tiles_per_chunk - 1) / G.tiles_per_chunk;
     G.grid = uint32_t(std::min<size_t>(resident, group_chunks[v]));
@@ -1246,7 +1399,7 @@ int ep_batch_launch(const ep_batch_plan* plan, void* stream) {
   for (uint32_t v = 0; v < kNumGroups; ++v) {
     const Group& G = P->groups[v];
     if (G.nchunks == 0) continue;
-    hipLaunchKernelGGL(kernel_of(v), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), tens,
+    hipLaunchKernelGGL(kernel_of(v, G.chains), dim3(G.grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream), tens,
                        chunks + G.chunk_begin, reinterpret_cast<uint32_t*>(wsb + P->ctr_off) + G.chunk_begin,
                        G.nchunks, G.tiles_per_chunk);
     hipError_t e = hipGetLastError();
