@@ -35,6 +35,10 @@
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// ring words are written as 32-bit pairs and read as 16-bit words: the stores go
+// through a type that may alias any other, so type-based alias analysis can
+// never move a ring read across the write of the words it reads
+typedef uint32_t __attribute__((may_alias)) u32_ring;
 
 namespace {
 
@@ -93,6 +97,10 @@ __host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
 __host__ __device__ constexpr bool has_split(int tl, uint32_t b) { return tl == kTabHybrid && b == 11; }
 __host__ __device__ constexpr size_t split_off_of(uint32_t b) { return table_bytes_of(kTabWorkspace, b); }
 __host__ __device__ constexpr size_t split_bytes_of(uint32_t b) { return (size_t(16) << b) * 4; }
+// packed layout: the byte-entry tables of fields 1..7 (when the tensor can use
+// them) follow the 16 packed tables in the workspace
+__host__ __device__ constexpr size_t byte_off_of(uint32_t b) { return size_t(16) << (b + 2); }
+__host__ __device__ constexpr size_t byte_bytes_of(uint32_t b) { return size_t(14) << (b + 2); }
 __host__ __device__ constexpr size_t storage_bytes_of(int tl, uint32_t b) {
   return table_bytes_of(tl, b) + (has_split(tl, b) ? split_bytes_of(b) : 0);
 }
@@ -122,6 +130,9 @@ struct alignas(16) DevTensor {
   uint32_t tpc;              // tiles per chunk of the tensor's launch group
   uint32_t direct;           // packed layouts: entries hold the value 2 z + c - 2 dmin (see kvals)
   uint32_t split;            // hybrid layout: 1 = per-slot entries usable (cleared by the build if some f > 127)
+  uint32_t byte_cand;        // packed layout: the workspace holds byte-entry tables for fields 1..7 (set by the host)
+  uint32_t bytev;            // ... and they are usable (cleared by the build if some f > 255)
+  uint32_t kbyte[4];         // byte entries: fp16 pairs (2 dmin_f - 1024) for fields (1,2), (3,4), (5,6), (-,7)
   int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
   uint64_t payload_words;
   const float* row_scales;
@@ -209,6 +220,10 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   unsigned char* lut8 = T.tab + (size_t(t) << b);
   uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
   uint32_t* lut32 = reinterpret_cast<uint32_t*>(T.tab) + (size_t(t) << b);
+  // byte entries of fields 1..7: f | (slot - cum) << 8 | fp16(1024 + n) << 16 with
+  // n = 2 z + c - 2 dmin_f (the value relative to the field's smaller minimum)
+  const bool bywrite = T.byte_cand != 0 && field <= 7;
+  uint32_t* lutb = reinterpret_cast<uint32_t*>(T.tab + byte_off_of(b)) + (size_t(t) << b);
   const size_t lb = lut_bytes_of(tl, b);
   uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
   float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
@@ -223,8 +238,10 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   }
   if (A == 0) {   // empty table: never used, the decoder flags the tile
     for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
-      if (is_packed(tl)) lut32[j] = 1u << 11;      // f = 1, slot - cum = 0, symbol 0
-      else if (tl == kTabNarrow) lut8[j] = 0;
+      if (is_packed(tl)) {
+        lut32[j] = 1u << 11;                          // f = 1, slot - cum = 0, symbol 0
+        if (bywrite) lutb[j] = 1u | (0x6400u << 16);  // f = 1, slot - cum = 0, n = 0
+      } else if (tl == kTabNarrow) lut8[j] = 0;
       else lut16[j] = 0;
       if (split) {
         fd16[j] = 1;                                // f = 1, slot - cum = 0
@@ -265,7 +282,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     __syncthreads();
   }
   // slot j -> largest i with cum_i <= j (a zero-frequency symbol is never chosen)
-  int big = 0;
+  int big = 0, big8 = 0;
   for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
     uint32_t lo = 0, hi = A;
     while (hi - lo > 1) {
@@ -284,6 +301,12 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         top = uint32_t((field < 8 || T.f8z8 ? 2 * d : 4 * d) + int32_t(c)) << 22;
       }
       lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | top;
+      if (bywrite) {
+        const uint32_t f = e & 0xFFFFu;
+        const uint32_t n = uint32_t(2 * (int32_t(lo) + mn - T.dmin[field]) + int32_t(c));   // < 1024: checked on the host
+        big8 |= f > 255u;
+        lutb[j] = (f & 0xFFu) | ((j - (e >> 16)) << 8) | ((0x6400u | n) << 16);
+      }
     } else if (tl == kTabNarrow) {
       lut8[j] = uint8_t(lo);
     } else {
@@ -300,6 +323,8 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   }
   // per-slot entries hold f in 7 bits: any larger frequency disables them for the tensor
   if (__syncthreads_or(big) && threadIdx.x == 0) atomicAnd(&T.split, 0u);
+  // byte entries hold f in 8 bits: any larger frequency disables them for the tensor
+  if (__syncthreads_or(big8) && threadIdx.x == 0) atomicAnd(&T.bytev, 0u);
 }
 
 // ---------------------------------------------------------------- container rounding
@@ -387,6 +412,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
+// Byte entries (see build_tables_kernel): the state update f * q + (slot - cum)
+// with f and slot - cum taken straight from bytes 0 and 1 of the entry by the
+// sub-dword operand selects of gfx950's VOP2 encoding, two instructions.
+__device__ __forceinline__ uint32_t mul_byte0(uint32_t e, uint32_t q) {
+  uint32_t r;
+  asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0 src1_sel:DWORD"
+      : "=v"(r) : "v"(e), "v"(q));
+  return r;
+}
+__device__ __forceinline__ uint32_t add_byte1(uint32_t e, uint32_t a) {
+  uint32_t r;
+  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+      : "=v"(r) : "v"(e), "v"(a));
+  return r;
+}
+// fp32(v * h) for the fp16 value v in the low (HI = false) or high half of p:
+// one fused mixed-precision multiply-add with the addend -0, which rounds the
+// exact product once and keeps the sign of a zero product, as a plain fp32
+// multiply of float(v) by h does.
+template <bool HI>
+__device__ __forceinline__ float mul_f16_f32(uint32_t p, float h) {
+  float r;
+  if (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(p), "v"(h), "s"(-0.0f));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(p), "v"(h), "s"(-0.0f));
+  return r;
+}
+typedef _Float16 h16x2_t __attribute__((ext_vector_type(2)));
+// exact fp16 additions: (1024 + n) + (2 dmin - 1024) = 2 z + c, both halves
+__device__ __forceinline__ uint32_t add_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h16x2_t, a) + __builtin_bit_cast(h16x2_t, b));
+}
+
 // Decode the 2*CH consecutive tiles tile0 .. tile0 + 2*CH - 1 of one wave (those
 // below tile_end).  Chain c of the wave is the tile pair tile0 + 2c, tile0 + 2c + 1,
 // one tile per half-wave; lane l of a half owns the tile's rANS state l.  The CH
@@ -397,8 +456,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // BT is the probability precision when known at compile time (0: read T.b),
 // TL the table layout (LDS tables start at LDS address 0), OK the output kind,
 // SP (hybrid layout) whether the per-slot entry maps are the ones staged in
-// LDS, CH the number of chains.  `rings` points to this wave's 2*CH rings.
-template <int BT, int TL, int OK, bool SP, int CH>
+// LDS, CH the number of chains, BY (packed layout) whether fields 1..7 use the
+// byte entries.  `rings` points to this wave's 2*CH rings.
+template <int BT, int TL, int OK, bool SP, int CH, bool BY>
 __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
                                              const unsigned char* __restrict__ lds,
                                              uint16_t* __restrict__ rings) {
@@ -512,6 +572,11 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
   const uint32_t fw = kWide || direct ? 11u : 12u;           // width of f in the entry
   float kd[7] = {0, 0, 0, 0, 0, 0, 0}, k8d = 0.0f;
   int32_t m8d = 0;
+  uint32_t kb[4] = {0, 0, 0, 0};
+  if (BY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kb[i] = T.kbyte[i];
+  }
   if (kDirectable) {
 #pragma unroll
     for (int f = 0; f < 7; ++f) kd[f] = __builtin_bit_cast(float, T.kvals[18 + f]);
@@ -535,7 +600,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       // bits (tile payloads stay below 2^16 words)
       if (__builtin_amdgcn_inverse_ballot_w64(half_mask(w0, w1))) {
         const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
-        *reinterpret_cast<uint32_t*>(ring + ((F + lane2) & (kRingWords - 1u))) = pf[c];
+        *reinterpret_cast<u32_ring*>(ring + ((F + lane2) & (kRingWords - 1u))) = pf[c];
       }
       F0[c] += w0 ? kChunkWords : 0u;
       F1[c] += w1 ? kChunkWords : 0u;
@@ -547,7 +612,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       if (__builtin_amdgcn_inverse_ballot_w64(half_mask(c0, c1))) {
         const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
         const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rP, chunk_lane[c] + 2u * F, 0, 0);
-        *reinterpret_cast<uint32_t*>(ring + ((F + lane2) & (kRingWords - 1u))) = v;
+        *reinterpret_cast<u32_ring*>(ring + ((F + lane2) & (kRingWords - 1u))) = v;
       }
       F0[c] += c0 ? kChunkWords : 0u;
       F1[c] += c1 ? kChunkWords : 0u;
@@ -593,6 +658,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
     bool active[CH];
     uint32_t x_saved[CH], cs[CH];
     float vv[CH][9];
+    float yb[CH][7];                                          // byte entries: the products of fields 1..7
     float rv[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -643,7 +709,8 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           const uint32_t q = x[c] >> B;
-          x[c] = __umul24(__builtin_amdgcn_ubfe(e[c], 11, fw), q) + (e[c] & 0x7FFu);
+          if (BY && f <= 7) x[c] = add_byte1(e[c], mul_byte0(e[c], q));
+          else x[c] = __umul24(__builtin_amdgcn_ubfe(e[c], 11, fw), q) + (e[c] & 0x7FFu);
           ev[c][f] = e[c];
         }
         if (f == 5) {
@@ -660,7 +727,38 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       }
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        if (kDirectable && direct) {
+        if constexpr (BY) {
+          // byte entries: the high halves hold fp16(1024 + 2 (z - dmin) + c);
+          // pairs of them gathered by one permute and shifted by the fields'
+          // constants 2 dmin - 1024 in one packed fp16 add are 2 z + c exactly,
+          // and fed as fp16 to the multiply by the row scale.  Bit 17 of an
+          // entry (bit 1 of n) is the parity of z - dmin, as bit 23 of a direct
+          // entry, so the parity and field 8 follow the direct form.
+          const uint32_t p12 = add_f16x2(__builtin_amdgcn_perm(ev[c][2], ev[c][1], 0x07060302u), kb[0]);
+          const uint32_t p34 = add_f16x2(__builtin_amdgcn_perm(ev[c][4], ev[c][3], 0x07060302u), kb[1]);
+          const uint32_t p56 = add_f16x2(__builtin_amdgcn_perm(ev[c][6], ev[c][5], 0x07060302u), kb[2]);
+          const uint32_t p77 = add_f16x2(ev[c][7], kb[3]);
+          const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+              __builtin_amdgcn_bitop3_b32(ev[c][1], ev[c][2], ev[c][3], 0x96),
+              __builtin_amdgcn_bitop3_b32(ev[c][4], ev[c][5], ev[c][6], 0x96), ev[c][7], 0x96);
+          par[c] = __builtin_amdgcn_ubfe(x3, 17, pw);
+          const int32_t u8 = __mul24(int32_t(par[c]), m8d) +
+                             int32_t(__builtin_amdgcn_alignbit(0x4B400000u >> 10, ev[c][8], 22));
+          vv[c][8] = __builtin_bit_cast(float, u8) + k8d;
+          // slow rows: the value is halved first (exactly), then multiplied by g
+          const float hv = slow_rows ? 0.5f : rv[c];
+          yb[c][0] = mul_f16_f32<false>(p12, hv);
+          yb[c][1] = mul_f16_f32<true>(p12, hv);
+          yb[c][2] = mul_f16_f32<false>(p34, hv);
+          yb[c][3] = mul_f16_f32<true>(p34, hv);
+          yb[c][4] = mul_f16_f32<false>(p56, hv);
+          yb[c][5] = mul_f16_f32<true>(p56, hv);
+          yb[c][6] = mul_f16_f32<true>(p77, hv);
+          if (slow_rows) {
+#pragma unroll
+            for (int i = 0; i < 7; ++i) yb[c][i] = __fmul_rn(yb[c][i], rv[c]);
+          }
+        } else if (kDirectable && direct) {
           // direct entries: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 +
           // (2 z + c - 2 dmin), and one constant per field (the same for both
           // cosets) turns it into 2 z + c.  Bit 23 of an entry is the parity of
@@ -822,11 +920,17 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
         // slow rows: rv is g and 2 z + c is halved first (exactly)
         if (slow_rows) {
 #pragma unroll
-          for (int i = 1; i <= 8; ++i) v[i] = __fmul_rn(v[i], 0.5f);
+          for (int i = BY ? 8 : 1; i <= 8; ++i) v[i] = __fmul_rn(v[i], 0.5f);
         }
         float y[8];
+        if constexpr (BY) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(v[i + 1], rv[c]);
+          for (int i = 0; i < 7; ++i) y[i] = yb[c][i];
+          y[7] = __fmul_rn(v[8], rv[c]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(v[i + 1], rv[c]);
+        }
         if (OK == kOutBF16) {
           const u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                            pack_bf16x2(y[6], y[7])};
@@ -923,11 +1027,21 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     if (threadIdx.x == 0) __hip_atomic_store(ctr + ci, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // hybrid layout: the per-slot entry maps when the build kept them, else the slot maps
     const bool split = has_split(TL, BT) && T.split != 0;
+    // packed layout: the byte entries of fields 1..7 when the build kept them
+    constexpr bool kByteOk = TL == kTabPacked && OK != kOutLattice;
+    const bool bytev = kByteOk && T.bytev != 0;
     if (TL != kTabWorkspace) {
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)(T.tab + (split ? split_off_of(BT) : 0));
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
       const uint32_t n16 = uint32_t((has_split(TL, BT) && !split ? lut_bytes_of(TL, BT) : kTab) / 16u);
-      for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = src[i];
+      if (kByteOk && bytev) {
+        // fields 1..7 from the byte tables, field 8 (same offset) from the packed ones
+        const EP_GLOBAL u32x4* srcb = (const EP_GLOBAL u32x4*)(T.tab + byte_off_of(BT));
+        const uint32_t nb16 = uint32_t(byte_bytes_of(BT) / 16u);
+        for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = i < nb16 ? srcb[i] : src[i];
+      } else {
+        for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = src[i];
+      }
     }
     __syncthreads();
     // the first group of each wave is its own index, which spreads a short run
@@ -936,10 +1050,13 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     while (gr < ngroups) {
       if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
       if constexpr (has_split(TL, BT)) {
-        if (split) decode_tiles<BT, TL, OK, true, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else decode_tiles<BT, TL, OK, false, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        if (split) decode_tiles<BT, TL, OK, true, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+      } else if constexpr (kByteOk) {
+        if (bytev) decode_tiles<BT, TL, OK, false, CH, true>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       } else {
-        decode_tiles<BT, TL, OK, false, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       }
       gr = __builtin_amdgcn_readfirstlane(nx);
     }
@@ -1005,6 +1122,7 @@ struct Layout {
   size_t tens_off, chunk_off, ctr_off, total;
   std::vector<size_t> tab_off, tab_bytes, row_off;
   std::vector<uint32_t> variant, group;
+  std::vector<char> byte_cand;
   size_t max_chunks;                  // chunk slots for the smallest chunk (2 tiles)
   size_t group_tiles[kNumGroups];
 };
@@ -1044,6 +1162,52 @@ int validate(const ep_tensor_desc& d, int i) {
   return EP_OK;
 }
 
+// Direct entries (packed layout): each field's values over both cosets must fit
+// the entry's 10 top bits as 2 (z - dmin) + c (4 (m - dmin) + c for field 8), and
+// no table may be a one-symbol table at b = 11 (f = 2^11).  Fills dmin[1..8]
+// with each field's smaller minimum over the two cosets.
+bool direct_minima(const ep_tensor_desc& d, uint32_t variant, int32_t dmin[9]) {
+  bool direct = layout_of(variant) == kTabPacked;
+  const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
+  dmin[0] = 0;
+  for (int f = 1; f <= 8; ++f) {
+    int64_t mn = 0, mx = -1;
+    for (int c = 0; c < 2; ++c) {
+      const int k = 1 + 2 * (f - 1) + c;
+      if (d.alphabet[k] == 0) continue;
+      if (d.prob_bits == 11 && d.alphabet[k] == 1) direct = false;   // f = 2^11
+      const int64_t lo = d.min_offset[k], hi = lo + d.alphabet[k] - 1;
+      if (mx < mn) mn = lo, mx = hi;
+      else mn = std::min(mn, lo), mx = std::max(mx, hi);
+    }
+    if (mx < mn) mn = mx = 0;
+    if ((f < 8 ? 2 : k8) * (mx - mn) + 1 > 1023) direct = false;
+    dmin[f] = int32_t(mn);
+  }
+  return direct;
+}
+
+// Byte entries for fields 1..7 (the table build still checks every f < 256):
+// direct entries, with every field's smaller minimum within +-512, so that the
+// fp16 constants 2 dmin - 1024, the values 1024 + n and 2 z + c are all exact.
+bool byte_candidate(const ep_tensor_desc& d, uint32_t variant) {
+  int32_t dmin[9];
+  if (!direct_minima(d, variant, dmin)) return false;
+  for (int f = 1; f <= 7; ++f)
+    if (dmin[f] < -512 || dmin[f] > 512) return false;
+  return true;
+}
+
+// IEEE binary16 bits of an integer v, |v| <= 2048 (exactly representable)
+uint32_t f16_bits_of_int(int32_t v) {
+  if (v == 0) return 0;
+  const uint32_t s = v < 0 ? 0x8000u : 0u;
+  const uint32_t a = uint32_t(v < 0 ? -v : v);
+  const int e = 31 - __builtin_clz(a);                        // a in [2^e, 2^(e+1)), e <= 11
+  const uint32_t m = (e <= 10 ? (a << (10 - e)) : (a >> (e - 10))) & 0x3FFu;
+  return s | (uint32_t(e + 15) << 10) | m;
+}
+
 int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L) {
   if (n < 0 || (n > 0 && !descs)) return fail(EP_ERR_INVALID_ARG, "bad tensor count or NULL descriptors");
   size_t off = 0;
@@ -1055,6 +1219,7 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   L.row_off.resize(n);
   L.variant.resize(n);
   L.group.resize(n);
+  L.byte_cand.resize(n);
   for (uint32_t v = 0; v < kNumGroups; ++v) L.group_tiles[v] = 0;
   for (int i = 0; i < n; ++i) {
     int rc = validate(descs[i], i);
@@ -1065,6 +1230,8 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
     L.tab_bytes[i] = storage_bytes_of(layout_of(L.variant[i]), d.prob_bits);
+    L.byte_cand[i] = byte_candidate(d, L.variant[i]) ? 1 : 0;
+    if (L.byte_cand[i]) L.tab_bytes[i] += byte_bytes_of(d.prob_bits);
     L.max_chunks += (d.num_tiles + 1) / 2;
     L.group_tiles[L.group[i]] += d.num_tiles;
   }
@@ -1310,39 +1477,32 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     const uint32_t psh = wide ? 22 : 23;
     D.kvals[16] = (kpar & 1u) << psh;
     D.kvals[17] = ((kpar >> 1) & 1u) << psh;
-    // direct entries (packed layout): each field's values over both cosets
-    // must fit the entry's 10 top bits as 2 (z - dmin) + c (4 (m - dmin) + c
-    // for field 8), and every f must fit 11 bits
+    // direct entries (packed layout): uniform value constants per field
     {
-      bool direct = layout_of(L.variant[i]) == kTabPacked;
-      int64_t dsum = 0;
+      const bool direct = direct_minima(d, L.variant[i], D.dmin);
       const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
-      for (int f = 1; f <= 8; ++f) {
-        int64_t mn = 0, mx = -1;
-        for (int c = 0; c < 2; ++c) {
-          const int k = 1 + 2 * (f - 1) + c;
-          if (d.alphabet[k] == 0) continue;
-          if (d.prob_bits == 11 && d.alphabet[k] == 1) direct = false;   // f = 2^11
-          const int64_t lo = d.min_offset[k], hi = lo + d.alphabet[k] - 1;
-          if (mx < mn) mn = lo, mx = hi;
-          else mn = std::min(mn, lo), mx = std::max(mx, hi);
-        }
-        if (mx < mn) mn = mx = 0;
-        if ((f < 8 ? 2 : k8) * (mx - mn) + 1 > 1023) direct = false;
-        D.dmin[f] = int32_t(mn);
-        if (f < 8) {
-          dsum += mn;
-          const float kf = -float(12582912 - 2 * mn);
-          std::memcpy(&D.kvals[18 + f - 1], &kf, 4);
-        }
+      int64_t dsum = 0;
+      for (int f = 1; f <= 7; ++f) {
+        dsum += D.dmin[f];
+        const float kf = -float(12582912 - 2 * int64_t(D.dmin[f]));
+        std::memcpy(&D.kvals[18 + f - 1], &kf, 4);
       }
-      D.dmin[0] = 0;
       // field 8: 2 z8 + c = v8 + k8 dmin8 + 2 par (coded m), par = p ^ parity(sum of dmin1..7)
       const int64_t kd8 = (d.field8 == EP_FIELD8_Z8) ? 0 : (dsum & 1);
       const float k8f = -float(12582912 - k8 * D.dmin[8] - 2 * kd8);
       std::memcpy(&D.kvals[25], &k8f, 4);
       D.kvals[26] = uint32_t(d.field8 == EP_FIELD8_Z8 ? 0 : (kd8 ? -2 : 2));
       D.direct = direct ? 1u : 0u;
+      // byte entries: the fp16 constants 2 dmin_f - 1024 of fields 1..7, in pairs
+      D.byte_cand = L.byte_cand[i] ? 1u : 0u;
+      D.bytev = D.byte_cand;
+      uint32_t kh[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (D.byte_cand)
+        for (int f = 1; f <= 7; ++f) kh[f] = f16_bits_of_int(2 * D.dmin[f] - 1024);   // in [-2048, 0]
+      D.kbyte[0] = kh[1] | (kh[2] << 16);
+      D.kbyte[1] = kh[3] | (kh[4] << 16);
+      D.kbyte[2] = kh[5] | (kh[6] << 16);
+      D.kbyte[3] = kh[7] << 16;
     }
     // hybrid at b = 11: per-slot entries when every value 2 z + c (4 m + c) fits
     // 16 bits; the build clears the flag if some f > 127
