@@ -3,13 +3,13 @@
 Inputs are the benchmark's seeded tensors at their real shapes, compressed by
 the host encoder (pinned byte-identical to the oracle's encoder by
 test_host_encoder.py).  Every tensor of a set is decoded by one
-ep_decode_batch call, as bench.py does.  Small sets are compared whole against
-the oracle; for the large sets every tile status is checked and sampled tiles
-(first, last and random ones) are decoded by the oracle one by one and
-compared byte for byte.
+ep_decode_batch call, as bench.py does, and every tensor is compared whole,
+byte for byte, against the oracle's decode of the same container (the oracle
+runs on host threads, one tensor per thread).
 """
 import os
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -40,15 +40,19 @@ def _log(msg):
 
 
 def _encode(specs):
-    cts = []
-    t0 = time.time()
-    for i, s in enumerate(specs):
+    """Host-encode every spec; a few tensors at a time, each on a share of the threads."""
+    par = 4 if len(specs) >= 8 else 1
+    per = max(1, THREADS // par)
+
+    def one(s):
         W = s.weights(device="cuda").cpu().numpy()
-        cts.append(encoder.encode(W, s.target_bpp, V=s.vectors_per_tile or 0, b=s.prob_bits or 0,
-                                  route=s.route, threads=THREADS))
-        del W
-        if (i + 1) % 25 == 0:
-            _log(f"[fullsize] encoded {i + 1}/{len(specs)} ({time.time() - t0:.0f}s)")
+        return encoder.encode(W, s.target_bpp, V=s.vectors_per_tile or 0, b=s.prob_bits or 0,
+                              route=s.route, threads=per)
+
+    t0 = time.time()
+    with ThreadPoolExecutor(par) as pool:
+        cts = list(pool.map(one, specs))
+    _log(f"[fullsize] host-encoded {len(cts)} tensors in {time.time() - t0:.0f}s")
     return cts
 
 
@@ -62,36 +66,31 @@ def _decode_batch(cts, kinds):
     return outs
 
 
-def _flat(out, kind):
-    tv, nv = NP_VIEW[kind]
-    return out.view(tv).reshape(-1), nv
+def _compare_whole(cts, kinds, outs):
+    """Every tensor against the oracle, byte for byte; oracle decodes on host threads."""
+    def ref(i):
+        r, st = oracle.decode(cts[i], kinds[i])
+        return r, st
 
-
-def _check_sampled(cts, kinds, outs, per_tensor, rng):
-    bufs = {}
-    checked = 0
-    for ct, kind, out in zip(cts, kinds, outs):
-        if ct.T == 0:
-            continue
-        flat, nv = _flat(out, kind)
-        key = (ct.rows, ct.cols, kind)
-        if key not in bufs:
-            bufs[key] = np.zeros((ct.rows, ct.cols), nv)
-        ref = bufs[key]
-        picks = {0, ct.T - 1} | set(rng.integers(0, ct.T, size=per_tensor).tolist())
-        nvec = ct.rows * ct.cols // 8
-        for t in sorted(picks):
-            _, st = oracle.decode(ct, kind, t, t + 1, out=ref)
-            assert st[t] == 0
-            a, b = 8 * t * ct.V, 8 * min((t + 1) * ct.V, nvec)
-            got = flat[a:b].cpu().numpy().view(nv)
-            exp = ref.reshape(-1)[a:b]
-            if not np.array_equal(got, exp):
-                bad = np.flatnonzero(got != exp)
-                raise AssertionError(f"{ct.rows}x{ct.cols} {kind} tile {t}: {bad.size} mismatches, "
-                                     f"first at weight {a + bad[0]}")
-            checked += 1
-    return checked
+    t0 = time.time()
+    weights = 0
+    with ThreadPoolExecutor(THREADS) as pool:
+        for lo in range(0, len(cts), 2 * THREADS):          # bounded number of references in flight
+            idx = list(range(lo, min(len(cts), lo + 2 * THREADS)))
+            for i, (r, st) in zip(idx, pool.map(ref, idx)):
+                ct, kind = cts[i], kinds[i]
+                assert np.all(st == 0), f"tensor {i}: oracle tile status {np.unique(st)}"
+                tv, nv = NP_VIEW[kind]
+                got = outs[i].view(tv).cpu().numpy().view(nv).reshape(ct.rows, ct.cols)
+                if not np.array_equal(got, r):
+                    bad = np.flatnonzero(got.reshape(-1) != r.reshape(-1))
+                    raise AssertionError(f"tensor {i} ({ct.rows}x{ct.cols}, b={ct.b}, {kind}): "
+                                         f"{bad.size} mismatches, first at weight {bad[0]} "
+                                         f"(tile {bad[0] // (8 * ct.V)})")
+                weights += ct.rows * ct.cols
+    _log(f"[fullsize] {len(cts)} tensors, {weights / 1e9:.3f} G weights bit-exact "
+         f"(oracle compare {time.time() - t0:.0f}s)")
+    return weights
 
 
 def test_w3840_every_target_whole_tensor():
@@ -106,30 +105,33 @@ def test_w3840_every_target_whole_tensor():
     _log(f"[fullsize] 3840x3840 at 4..8 bpp, precisions {bs}: whole tensors bit-exact")
 
 
-@pytest.mark.timeout(600)
-def test_dit_set_full_batch_sampled_tiles():
+@pytest.mark.timeout(900)
+def test_dit_set_whole_batch_bit_exact():
     specs = synthgen.workload("dit_linear_set_30x5_4bpp_bf16")
+    assert len(specs) == 150
     cts = _encode(specs)
-    outs = _decode_batch(cts, ["bf16"] * len(cts))
-    n = _check_sampled(cts, ["bf16"] * len(cts), outs, 3, np.random.default_rng(3))
-    _log(f"[fullsize] DiT set: {len(cts)} tensors, all tile statuses ok, {n} sampled tiles bit-exact")
+    kinds = ["bf16"] * len(cts)
+    outs = _decode_batch(cts, kinds)
+    assert _compare_whole(cts, kinds, outs) == sum(s.rows * s.cols for s in specs)
 
 
-@pytest.mark.timeout(300)
-def test_llm_fp8_route_two_layers_sampled_tiles():
-    specs = synthgen.workload("llm_prefill_16x5_fp8route_5bpp")[:10]
+@pytest.mark.timeout(900)
+def test_llm_fp8_set_whole_batch_bit_exact():
+    specs = synthgen.workload("llm_prefill_16x5_fp8route_5bpp")
+    assert len(specs) == 80
     cts = _encode(specs)
-    outs = _decode_batch(cts, ["fp8"] * len(cts))
-    n = _check_sampled(cts, ["fp8"] * len(cts), outs, 6, np.random.default_rng(4))
-    _log(f"[fullsize] LLM FP8 route: {len(cts)} tensors, {n} sampled tiles bit-exact")
+    kinds = ["fp8"] * len(cts)
+    outs = _decode_batch(cts, kinds)
+    assert _compare_whole(cts, kinds, outs) == sum(s.rows * s.cols for s in specs)
 
 
-@pytest.mark.timeout(300)
-def test_mixed_int8_route_subset_sampled_tiles():
-    specs = synthgen.workload("mixed_300_int8route_2or8bpp")[:60]
+@pytest.mark.timeout(900)
+def test_mixed_int8_set_whole_batch_bit_exact():
+    specs = synthgen.workload("mixed_300_int8route_2or8bpp")
+    assert len(specs) == 300
     assert any(s.target_bpp == 8.0 for s in specs) and any(s.target_bpp == 2.0 for s in specs)
     cts = _encode(specs)
-    outs = _decode_batch(cts, ["int8"] * len(cts))
-    n = _check_sampled(cts, ["int8"] * len(cts), outs, 4, np.random.default_rng(5))
-    _log(f"[fullsize] mixed INT8 route: {len(cts)} tensors (b {sorted({c.b for c in cts})}), "
-         f"{n} sampled tiles bit-exact")
+    assert len({c.b for c in cts}) >= 2                    # several probability precisions in one batch
+    kinds = ["int8"] * len(cts)
+    outs = _decode_batch(cts, kinds)
+    assert _compare_whole(cts, kinds, outs) == sum(s.rows * s.cols for s in specs)
