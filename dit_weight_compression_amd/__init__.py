@@ -25,7 +25,8 @@ TILE_OK, TILE_BAD_STATE, TILE_BAD_LENGTH, TILE_OVERRUN, TILE_EMPTY_TABLE = 0, 1,
 # every symbol include/entropack.h declares
 EXPORTS = ["ep_status_string", "ep_last_error", "ep_abi_version", "ep_workspace_size",
            "ep_decode_batch", "ep_decode_tensor", "ep_batch_prepare", "ep_batch_launch",
-           "ep_convert_f32"]
+           "ep_convert_f32", "ep_decode_batch_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20      # EP_NOALLOC_SCRATCH_BYTES
 # every symbol include/entropack_device_encode.h declares (same library)
 DEVICE_ENCODE_EXPORTS = ["ep_encode_device_workspace_size", "ep_encode_device",
                          "ep_encode_device_emit", "ep_encode_device_rdo_workspace_size",
@@ -94,6 +95,8 @@ def lib():
         L.ep_batch_launch.restype = C.c_int
         L.ep_convert_f32.argtypes = [vp, vp, C.c_uint64, C.c_int, vp]
         L.ep_convert_f32.restype = C.c_int
+        L.ep_decode_batch_noalloc.argtypes = [vp, vp, vp, vp, C.c_int, vp]
+        L.ep_decode_batch_noalloc.restype = C.c_int
         L.ep_encode_device_workspace_size.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_uint32,
                                                       C.c_int, C.POINTER(C.c_size_t)]
         L.ep_encode_device_workspace_size.restype = C.c_int
@@ -274,6 +277,31 @@ def decode_batch(packed: Sequence[PackedTensor], dtypes, outs=None, with_status:
     return outs, statuses
 
 
+def decode_batch_noalloc(packed: Sequence[PackedTensor], dtypes, outs, statuses=None, stream=None):
+    """Decode into caller-made outputs with ep_decode_batch_noalloc (the library's static scratch).
+
+    statuses: None or one int32 device tensor of at least max(T, 1) entries per tensor.
+    """
+    torch = _torch()
+    if isinstance(dtypes, str):
+        dtypes = [dtypes] * len(packed)
+    dev = packed[0].payload.device if packed else torch.device("cuda")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    n = len(packed)
+    descs = (EpTensorDesc * max(n, 1))(*[p.desc() for p in packed])
+    dt = (C.c_int * max(n, 1))(*[DTYPES[d] for d in dtypes])
+    outp = (C.c_void_p * max(n, 1))(*[o.data_ptr() for o in outs])
+    stp = None
+    if statuses is not None:
+        stp = (C.c_void_p * max(n, 1))(*[s.data_ptr() if s is not None else None for s in statuses])
+    _check(lib().ep_decode_batch_noalloc(C.cast(descs, C.c_void_p), C.cast(dt, C.c_void_p),
+                                         C.cast(outp, C.c_void_p),
+                                         None if stp is None else C.cast(stp, C.c_void_p), n,
+                                         C.c_void_p(stream.cuda_stream)))
+    return outs, statuses
+
+
 def decode_tensor(p: PackedTensor, dtype: str = "bf16", out=None, with_status: bool = False,
                   workspace=None, stream=None):
     """Decode one tensor with ep_decode_tensor; returns (out, status)."""
@@ -298,6 +326,7 @@ def decode_tensor(p: PackedTensor, dtype: str = "bf16", out=None, with_status: b
 # the C ABI names
 ep_decode_tensor = decode_tensor
 ep_decode_batch = decode_batch
+ep_decode_batch_noalloc = decode_batch_noalloc
 ep_workspace_size = workspace_size
 
 

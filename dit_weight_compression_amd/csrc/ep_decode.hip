@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1583,6 +1584,55 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
   void* outs[1] = {out};
   int32_t* sts[1] = {tile_status};
   return ep_decode_batch(desc, &dtype, outs, sts, 1, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of ep_decode_batch_noalloc: a device array the code object's
+// loader places on every GPU the library runs on, so the call allocates
+// nothing.  In host code `scratch` only names the array; its device address on
+// the current GPU comes from hipGetSymbolAddress, looked up once per device.
+static_assert(EP_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size must keep 256-byte alignment");
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(EP_ERR_UNSUPPORTED, "device index " + std::to_string(dev) + " beyond the static scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+      return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) gave a NULL or misaligned address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return EP_OK;
+}
+}  // namespace
+
+int ep_decode_batch_noalloc(const ep_tensor_desc* descs, const int* dtypes, void* const* outs,
+                            int32_t* const* tile_status, int n, void* stream) {
+  if (n > 0 && (!dtypes || !outs)) return fail(EP_ERR_INVALID_ARG, "NULL dtypes or outs");
+  Layout L;
+  int rc = make_layout(descs, dtypes, n, L);
+  if (rc != EP_OK) return rc;
+  if (L.total > size_t(EP_NOALLOC_SCRATCH_BYTES))
+    return fail(EP_ERR_WORKSPACE, "batch needs " + std::to_string(L.total) + " bytes of workspace; the static "
+                "scratch holds " + std::to_string(size_t(EP_NOALLOC_SCRATCH_BYTES)) +
+                " (split the batch, or call ep_decode_batch with a workspace)");
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != EP_OK) return rc;
+  return ep_decode_batch(descs, dtypes, outs, tile_status, n, ws, size_t(EP_NOALLOC_SCRATCH_BYTES), stream);
 }
 
 int ep_convert_f32(const float* in, void* out, uint64_t n, int dtype, void* stream) {

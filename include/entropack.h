@@ -155,6 +155,29 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
                      void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory: code recorded under stream
+ * capture, serving loops that must not allocate, harnesses that forbid
+ * hipMalloc.  ep_decode_batch with the library's own workspace, a static
+ * device array of EP_NOALLOC_SCRATCH_BYTES that every GPU the library runs on
+ * holds from the loading of the library's device code until the process ends.
+ * The call allocates no device memory; its address lookup happens once per
+ * device, on the first call with that device current.  Buffers and `stream`
+ * must belong to the current device.
+ *   Limit: batches whose ep_workspace_size() exceeds EP_NOALLOC_SCRATCH_BYTES
+ *   are rejected with EP_ERR_WORKSPACE before any GPU work (split them, or use
+ *   ep_decode_batch).
+ *   Sharing: all calls on one GPU use that GPU's one array, which keeps the
+ *   last call's contents; every byte a call reads there it has written first.
+ *   Calls that overlap on one GPU (on different streams, or from host threads
+ *   without ordering) race on the array and give undefined results: order
+ *   them on one stream.
+ * Other arguments, errors and tile statuses: as ep_decode_batch.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ep_decode_batch_noalloc(const ep_tensor_desc* descs, const int* dtypes, void* const* outs,
+                            int32_t* const* tile_status, int n, void* stream);
+
+/*
  * The two halves of ep_decode_batch, for callers that time the decode kernel
  * on its own.  ep_batch_prepare validates the arguments and enqueues the
  * upload of the schedule and the decode-table build; ep_batch_launch enqueues

@@ -129,6 +129,35 @@ def test_prepare_rejects_missing_plan_and_small_workspace():
     assert L.ep_batch_launch(C.byref(ep.EpBatchPlan()), None) == ep.EP_ERR_INVALID_ARG
 
 
+def test_noalloc_entry_point_rejects_batches_beyond_its_scratch():
+    # the checks run on the host before any HIP call: no GPU needed
+    L = ep.lib()
+    vp = C.c_void_p
+    d = _desc(rows=4096, cols=4096, V=32)
+    rc, one, _ = _ws_status(d)
+    assert rc == ep.EP_OK
+    n = ep.NOALLOC_SCRATCH_BYTES // one + 1
+    rc, total, _ = _ws_status(d, n)
+    assert rc == ep.EP_OK and total > ep.NOALLOC_SCRATCH_BYTES
+    arr = (ep.EpTensorDesc * n)(*([d] * n))
+    dt = (C.c_int * n)(*([0] * n))
+    outs = (C.c_void_p * n)(*([0x2000] * n))
+    rc = L.ep_decode_batch_noalloc(C.cast(arr, vp), C.cast(dt, vp), C.cast(outs, vp), None, n, None)
+    msg = L.ep_last_error().decode()
+    assert rc == ep.EP_ERR_WORKSPACE, (rc, msg)
+    assert str(total) in msg and str(ep.NOALLOC_SCRATCH_BYTES) in msg
+    # malformed arguments are refused the same way as by ep_decode_batch
+    assert L.ep_decode_batch_noalloc(C.cast(arr, vp), None, C.cast(outs, vp), None, 1, None) == ep.EP_ERR_INVALID_ARG
+    bad = _desc()
+    bad.cols = 12
+    arr1 = (ep.EpTensorDesc * 1)(bad)
+    assert L.ep_decode_batch_noalloc(C.cast(arr1, vp), C.cast(dt, vp), C.cast(outs, vp), None, 1,
+                                     None) == ep.EP_ERR_INVALID_ARG
+    text = open(os.path.join(ROOT, "include", "entropack.h")).read()
+    assert int(re.search(r"#define EP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(1)) << 20 \
+        == ep.NOALLOC_SCRATCH_BYTES
+
+
 def test_python_binding_has_no_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(ep, "_lib", None)
     monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
