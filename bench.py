@@ -227,11 +227,48 @@ def cpu_baseline(hosts, dtype: str, budget_s: float, threads: int):
     w1, s1, n1 = single(budget_s / 2)
     with cf.ThreadPoolExecutor(max_workers=threads) as pool:
         wn, sn, nn = multi(budget_s / 2, pool)
+    host = host_cpus()
     return {"value": wn / sn / 1e9, "unit": "Gweights/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "affinity_cpus": host["affinity_cpus"],
+            "host_logical_cpus": host["logical_cpus"], "host_physical_cores": host["physical_cores"],
+            "single_thread_value": w1 / s1 / 1e9,
             "sample": f"first {nn} tensor(s) of the workload ({wn} weights) decoded to {dtype} by the "
                       f"CPU oracle on {threads} threads over tile ranges in {sn:.1f}s; one thread: "
                       f"{n1} tensor(s), {w1} weights in {s1:.1f}s = {w1 / s1 / 1e9:.4f} Gweights/s; "
-                      f"host CPU: {_cpu_model()}"}
+                      f"host CPU: {_cpu_model()}, {host['physical_cores']} physical cores, "
+                      f"{host['logical_cpus']} logical CPUs, {host['affinity_cpus']} usable by this process"}
+
+
+def host_cpus() -> dict:
+    """Logical CPUs, the CPUs this process may run on, and physical cores (from /proc/cpuinfo)."""
+    logical = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = logical
+    cores = set()
+    try:
+        phys = core = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("physical id"):
+                    phys = line.split(":", 1)[1].strip()
+                elif line.startswith("core id"):
+                    core = line.split(":", 1)[1].strip()
+                elif not line.strip():
+                    if core is not None:
+                        cores.add((phys, core))
+                    phys = core = None
+        if core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"logical_cpus": logical, "affinity_cpus": affinity, "physical_cores": len(cores) or None}
+
+
+def default_threads() -> int:
+    """Every CPU this process may run on, up to the 16-CPU share a one-GPU job is given."""
+    return max(1, min(16, host_cpus()["affinity_cpus"]))
 
 
 def _cpu_model() -> str:
@@ -601,7 +638,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--max-tensors", type=int, default=0, help="use only the first N tensors")
-    ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--threads", type=int, default=default_threads(),
+                    help="host threads for the compressor and the CPU oracle baseline "
+                         "(default: the CPUs this process may use, at most 16)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-encoder", action="store_true",

@@ -137,7 +137,7 @@ struct alignas(16) DevTensor {
   int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
   uint64_t payload_words;
   const float* row_scales;
-  float* rowv;               // workspace: per row the pair (g/2, g), g = fp32(scale * row scale)
+  float* rowv;               // workspace: g/2 of rows 0..rows-1, then g of the same rows, g = fp32(scale * row scale)
   const uint32_t* states;
   const uint32_t* offsets;
   const uint16_t* payload;
@@ -189,8 +189,9 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   }
   if (blockIdx.x >= 16) {
     // per-row multipliers, 1024 rows per block: (2 z + c) * (g / 2) equals
-    // (z + c/2) * g exactly whenever g / 2 is exact; the pair (g/2, g) is
-    // stored and a tensor with any row where g / 2 is inexact uses g.
+    // (z + c/2) * g exactly whenever g / 2 is exact; g/2 and g are stored in
+    // two arrays (the decoder reads one of them, 4 bytes per row) and a
+    // tensor with any row where g / 2 is inexact uses g.
     const uint32_t r0 = (blockIdx.x - 16) * 1024u;
     bool inexact = false;
 #pragma unroll
@@ -200,7 +201,8 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         const float gr = __fmul_rn(T.scale, T.row_scales[r]);
         const float h = __fmul_rn(gr, 0.5f);
         inexact |= !(__fmul_rn(h, 2.0f) == gr);
-        reinterpret_cast<float2*>(T.rowv)[r] = make_float2(h, gr);
+        T.rowv[r] = h;
+        T.rowv[T.rows + r] = gr;
       }
     }
     if (inexact) atomicOr(&T.slow_rows, 1u);
@@ -491,7 +493,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
   // scalar registers; each lane keeps its half's ring read pointer (vP) so
   // that the renormalisation needs no scalar bookkeeping.
   uint32_t n[CH], x[CH], vP[CH], F0[CH], F1[CH], end0[CH], end1[CH], n0[CH], n1[CH];
-  uint32_t chunk_lane[CH], pf[CH], g[CH], rowb[CH], col[CH];
+  uint32_t chunk_lane[CH], endl[CH], pf[CH], g[CH], rowb[CH], col[CH];
   uint64_t empty_err[CH];
   bool bad_len[CH], tile_ok[CH];
   uint32_t kfull = ~0u, kmax = 0;
@@ -526,19 +528,23 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
     F1[c] = 0;
     empty_err[c] = 0;
     chunk_lane[c] = 2u * ((half ? a01 : a00) + lane2);       // byte offset of this lane's part
+    // chunks that start at word F: this lane's two words hold some of the
+    // tile's payload while F < endl (lanes past the tile's last word load
+    // nothing, so no cache line beyond the tile is fetched for them)
+    const uint32_t Eh = half ? end1[c] : end0[c];
+    endl[c] = Eh > lane2 ? Eh - lane2 : 0u;
     // the chunk held in registers is always the one starting at word F of the half
-    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, (half ? end1[c] : end0[c]) > 0u ? chunk_lane[c]
-                                                                                     : payload_bytes, 0, 0);
+    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, endl[c] > 0u ? chunk_lane[c] : payload_bytes, 0, 0);
     kfull = min(kfull, min(n0[c], n1[c]) >> 5);
     kmax = max(kmax, max((n0[c] + 31u) >> 5, (n1[c] + 31u) >> 5));
     g[c] = t * T.V + l;                                       // < 2^32: checked on the host
-    // rowb: byte offset of the row multiplier, g/2 or (slow rows) g of the row's pair
-    rowb[c] = slow_rows ? 4u : 0u;
+    // rowb: byte offset of the row multiplier, g/2 or (slow rows) g
+    rowb[c] = slow_rows ? 4u * T.rows : 0u;
     col[c] = 0;
     if (tile_ok[c]) {
       const uint32_t row = g[c] / vpr;
       col[c] = g[c] - row * vpr;
-      rowb[c] += 8u * row;
+      rowb[c] += 4u * row;
     }
   }
   // A store past the end of the output per chain (dropped by the hardware): it
@@ -612,15 +618,15 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       if (!(c0 || c1)) break;
       if (__builtin_amdgcn_inverse_ballot_w64(half_mask(c0, c1))) {
         const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
-        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rP, chunk_lane[c] + 2u * F, 0, 0);
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rP, F < endl[c] ? chunk_lane[c] + 2u * F
+                                                                                : payload_bytes, 0, 0);
         *reinterpret_cast<u32_ring*>(ring + ((F + lane2) & (kRingWords - 1u))) = v;
       }
       F0[c] += c0 ? kChunkWords : 0u;
       F1[c] += c1 ? kChunkWords : 0u;
     }
     const uint32_t F = __builtin_amdgcn_ubfe(F0[c] | (F1[c] << 16), hs, 16);
-    const uint32_t E = half ? end1[c] : end0[c];
-    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, F < E ? chunk_lane[c] + 2u * F : payload_bytes, 0, 0);
+    pf[c] = __builtin_amdgcn_raw_buffer_load_b32(rP, F < endl[c] ? chunk_lane[c] + 2u * F : payload_bytes, 0, 0);
   };
 
   // Renormalisation of every chain: the lanes of a half whose state fell below
@@ -960,10 +966,10 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       col[c] += 32u;
       if (col[c] >= vpr) {                  // rows of at least 32 vectors wrap at most once
         col[c] -= vpr;
-        rowb[c] += 8u;
+        rowb[c] += 4u;
         while (col[c] >= vpr) {
           col[c] -= vpr;
-          rowb[c] += 8u;
+          rowb[c] += 4u;
         }
       }
     }
