@@ -173,8 +173,37 @@ int fail(int code, const std::string& msg) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- table build
+// Exclusive scan (sum or max, identity 0) of one value per thread over a
+// 256-thread block: a shuffle scan inside each wave, then the wave totals.
+template <bool kMax>
+__device__ __forceinline__ uint32_t block_scan256_excl(uint32_t v, uint32_t* __restrict__ part) {
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (uint32_t d = 1; d < 64; d <<= 1) {
+    const uint32_t u = uint32_t(__shfl_up(int(incl), d, 64));
+    if (lane >= d) incl = kMax ? max(incl, u) : incl + u;
+  }
+  if (lane == 63u) part[w] = incl;
+  uint32_t ex = uint32_t(__shfl_up(int(incl), 1u, 64));
+  if (lane == 0u) ex = 0u;
+  __syncthreads();
+  uint32_t pre = 0;
+  for (uint32_t i = 0; i < w; ++i) pre = kMax ? max(pre, part[i]) : pre + part[i];
+  __syncthreads();                               // part is reusable after this
+  return kMax ? max(pre, ex) : pre + ex;
+}
+
+// Dynamic LDS of the table build: the slot marks (M u16) and the table's
+// frequencies (A u16) of the largest table in the batch.
+constexpr size_t build_lds_bytes(uint32_t max_b, uint32_t max_alphabet) {
+  return ((size_t(2) << max_b) + 2u * size_t(max_alphabet) + 15u) / 16u * 16u;
+}
+
 // One block per (coordinate table, tensor): cumulative frequencies by a block
-// scan, then the slot -> symbol map by a binary search per slot.
+// scan over per-thread symbol ranges; every symbol with f > 0 marks the slot
+// where its interval starts, and a forward scan over the slots carries the
+// last mark, which is the slot's symbol (a zero-frequency symbol never marks).
 __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens, Chunk* __restrict__ chunks,
                                                           uint32_t row_blocks) {
   DevTensor& T = tens[blockIdx.y];
@@ -230,9 +259,10 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   const size_t lb = lut_bytes_of(tl, b);
   uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
   float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
-  __shared__ uint32_t scan[256];
-  __shared__ uint32_t cums[1024];              // packed layouts: f | cum << 16 per symbol
-  __shared__ uint32_t carry;
+  extern __shared__ uint16_t build_lds[];
+  uint16_t* mark = build_lds;                  // per slot: 1 + the symbol whose interval starts there, else 0
+  uint16_t* fl = build_lds + M;                // the table's frequencies
+  __shared__ uint32_t part[4];
   if (!is_packed(tl)) {
     for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
       sym[i] = 0;
@@ -253,49 +283,51 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     }
     return;
   }
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
   const uint16_t* fr = T.freqs + T.freq_base[k];
   const int32_t mn = T.minv[k];
-  for (uint32_t base = 0; base < A; base += blockDim.x) {
-    const uint32_t i = base + threadIdx.x;
-    const uint32_t f = i < A ? fr[i] : 0u;
-    scan[threadIdx.x] = f;
-    __syncthreads();
-    for (uint32_t off = 1; off < blockDim.x; off <<= 1) {   // inclusive Hillis-Steele scan
-      uint32_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0u;
-      __syncthreads();
-      scan[threadIdx.x] += v;
-      __syncthreads();
-    }
-    const uint32_t cum = carry + scan[threadIdx.x] - f;
-    if (i < A) {
-      if (is_packed(tl)) {
-        cums[i] = (f & 0xFFFFu) | (cum << 16);
-      } else {
+  for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) mark[j] = 0;
+  for (uint32_t i = threadIdx.x; i < A; i += blockDim.x) fl[i] = fr[i];
+  __syncthreads();
+  // cumulative frequencies: thread tid owns the symbols [tid Q, tid Q + Q)
+  {
+    const uint32_t Q = (A + 255u) / 256u;
+    const uint32_t i0 = min(A, threadIdx.x * Q), i1 = min(A, i0 + Q);
+    uint32_t sum = 0;
+    for (uint32_t i = i0; i < i1; ++i) sum += fl[i];
+    uint32_t cum = block_scan256_excl<false>(sum, part);
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t f = fl[i];
+      if (f > 0u && cum < M) mark[cum] = uint16_t(i + 1u);       // distinct slots: cum grows with f > 0
+      if (!is_packed(tl)) {
         // the narrow layout (b = 12, f <= 4096) keeps the parity of the value z in bit 15
         const uint32_t zpar = (tl == kTabNarrow && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
         sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
         const int32_t z = int32_t(i) + mn;
         val[i] = float(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
       }
+      cum += f;
     }
-    __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) carry += scan[threadIdx.x];
-    __syncthreads();
   }
-  // slot j -> largest i with cum_i <= j (a zero-frequency symbol is never chosen)
+  __syncthreads();
+  // slot j -> the last mark at or below it: thread tid owns the slots [tid R, tid R + R)
+  const uint32_t R = M / 256u;
+  const uint32_t j0 = threadIdx.x * R;
+  uint32_t last = 0;                           // (slot + 1) << 16 | (symbol + 1) of a mark
+  for (uint32_t q = 0; q < R; ++q) {
+    const uint32_t mk = mark[j0 + q];
+    if (mk) last = ((j0 + q + 1u) << 16) | mk;
+  }
+  uint32_t key = block_scan256_excl<true>(last, part);
   int big = 0, big8 = 0;
-  for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
-    uint32_t lo = 0, hi = A;
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) >> 1;
-      const uint32_t cm = is_packed(tl) ? (cums[mid] >> 16) : (sym[mid] >> 16) - (c << b);
-      if (cm <= j) lo = mid;
-      else hi = mid;
-    }
+  for (uint32_t q = 0; q < R; ++q) {
+    const uint32_t j = j0 + q;
+    const uint32_t mk = mark[j];
+    if (mk) key = ((j + 1u) << 16) | mk;
+    // with sum f = M slot 0 always holds a mark; a table without one decodes garbage, in bounds
+    const uint32_t lo = key ? (key & 0xFFFFu) - 1u : 0u;
+    const uint32_t cum = key ? (key >> 16) - 1u : 0u;
+    const uint32_t f = fl[lo];
     if (is_packed(tl)) {
-      const uint32_t e = cums[lo];
       // the entry's top bits: the symbol index, or (direct entries) the value
       // 2 z + c (4 m + c for field 8) relative to the field's smaller minimum
       uint32_t top = lo << (tl == kTabPacked ? 23 : 22);
@@ -303,24 +335,24 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         const int32_t d = int32_t(lo) + mn - T.dmin[field];
         top = uint32_t((field < 8 || T.f8z8 ? 2 * d : 4 * d) + int32_t(c)) << 22;
       }
-      lut32[j] = (j - (e >> 16)) | ((e & 0xFFFFu) << 11) | top;
+      lut32[j] = (j - cum) | ((f & 0xFFFFu) << 11) | top;
       if (bywrite) {
-        const uint32_t f = e & 0xFFFFu;
         const uint32_t n = uint32_t(2 * (int32_t(lo) + mn - T.dmin[field]) + int32_t(c));   // < 1024: checked on the host
         big8 |= f > 255u;
-        lutb[j] = (f & 0xFFu) | ((j - (e >> 16)) << 8) | ((0x6400u | n) << 16);
+        lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | ((0x6400u | n) << 16);
       }
     } else if (tl == kTabNarrow) {
       lut8[j] = uint8_t(lo);
     } else {
       lut16[j] = uint16_t(lo);
       if (split) {
-        const uint32_t e = sym[lo];
-        const uint32_t f = e & 0xFFFFu, d = j - ((e >> 16) - (c << b));
-        const uint32_t zp = field < 8 ? (uint32_t(int32_t(lo) + mn) & 1u) : 0u;
+        const uint32_t d = j - cum;
+        const int32_t z = int32_t(lo) + mn;
+        const uint32_t zp = field < 8 ? (uint32_t(z) & 1u) : 0u;
         big |= f > 127u;
         fd16[j] = uint16_t((f & 0x7Fu) | (d << 7) | (zp << 15));
-        sval[j] = int16_t(val[lo]);                  // |value| < 2^15: checked on the host
+        // |value| < 2^15: checked on the host
+        sval[j] = int16_t(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
       }
     }
   }
@@ -1543,7 +1575,14 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     uint64_t max_rows = 1;
     for (int i = 0; i < n; ++i) max_rows = std::max<uint64_t>(max_rows, uint64_t(descs[i].rows));
     const uint32_t row_blocks = uint32_t((max_rows + 1023) / 1024);
-    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks + chunk_blocks, n), dim3(256), 0, st,
+    uint32_t max_b = 9, max_a = 0;
+    for (int i = 0; i < n; ++i) {
+      if (descs[i].num_tiles == 0) continue;
+      max_b = std::max(max_b, descs[i].prob_bits);
+      for (int k = 1; k < kTables; ++k) max_a = std::max(max_a, descs[i].alphabet[k]);
+    }
+    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks + chunk_blocks, n), dim3(256),
+                       uint32_t(build_lds_bytes(max_b, max_a)), st,
                        reinterpret_cast<DevTensor*>(wsb + L.tens_off), reinterpret_cast<Chunk*>(wsb + L.chunk_off),
                        row_blocks);
     e = hipGetLastError();
