@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -98,10 +99,12 @@ __host__ __device__ constexpr size_t table_bytes_of(int tl, uint32_t b) {
 __host__ __device__ constexpr bool has_split(int tl, uint32_t b) { return tl == kTabHybrid && b == 11; }
 __host__ __device__ constexpr size_t split_off_of(uint32_t b) { return table_bytes_of(kTabWorkspace, b); }
 __host__ __device__ constexpr size_t split_bytes_of(uint32_t b) { return (size_t(16) << b) * 4; }
-// packed layout: the byte-entry tables of fields 1..7 (when the tensor can use
-// them) follow the 16 packed tables in the workspace
+// packed and wide layouts: the byte-entry tables (when the tensor can use them)
+// follow the 16 packed tables in the workspace: fields 1..7 in the fp16 form,
+// or all 16 tables in the i16 form (see DevTensor::byte_cand)
 __host__ __device__ constexpr size_t byte_off_of(uint32_t b) { return size_t(16) << (b + 2); }
 __host__ __device__ constexpr size_t byte_bytes_of(uint32_t b) { return size_t(14) << (b + 2); }
+__host__ __device__ constexpr size_t byte16_bytes_of(uint32_t b) { return size_t(16) << (b + 2); }
 __host__ __device__ constexpr size_t storage_bytes_of(int tl, uint32_t b) {
   return table_bytes_of(tl, b) + (has_split(tl, b) ? split_bytes_of(b) : 0);
 }
@@ -131,7 +134,9 @@ struct alignas(16) DevTensor {
   uint32_t tpc;              // tiles per chunk of the tensor's launch group
   uint32_t direct;           // packed layouts: entries hold the value 2 z + c - 2 dmin (see kvals)
   uint32_t split;            // hybrid layout: 1 = per-slot entries usable (cleared by the build if some f > 127)
-  uint32_t byte_cand;        // packed layout: the workspace holds byte-entry tables for fields 1..7 (set by the host)
+  uint32_t byte_cand;        // byte-entry tables in the workspace (set by the host): 0 none; 1 fields 1..7 as
+                             // f | (slot - cum) << 8 | fp16(1024 + 2 (z - dmin) + c) << 16 (direct packed
+                             // tensors); 2 all 16 tables as f | (slot - cum) << 8 | i16 value << 16
   uint32_t bytev;            // ... and they are usable (cleared by the build if some f > 255)
   uint32_t kbyte[4];         // byte entries: fp16 pairs (2 dmin_f - 1024) for fields (1,2), (3,4), (5,6), (-,7)
   int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
@@ -157,6 +162,14 @@ struct alignas(16) DevTensor {
   uint32_t freq_base[kTables];
   uint32_t alphabet[kTables];
 };
+
+// The layout checks in the tests read these fields of the workspace copy
+// (descriptor i at byte i * sizeof(DevTensor)) back after ep_batch_prepare.
+static_assert(sizeof(DevTensor) == 560, "DevTensor layout read by the tests");
+static_assert(offsetof(DevTensor, variant) == 36 && offsetof(DevTensor, slow_rows) == 56 &&
+                  offsetof(DevTensor, direct) == 72 && offsetof(DevTensor, split) == 76 &&
+                  offsetof(DevTensor, byte_cand) == 80 && offsetof(DevTensor, bytev) == 84,
+              "DevTensor layout read by the tests");
 
 struct Chunk {
   uint32_t tensor;
@@ -252,9 +265,11 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   unsigned char* lut8 = T.tab + (size_t(t) << b);
   uint16_t* lut16 = reinterpret_cast<uint16_t*>(T.tab) + (size_t(t) << b);
   uint32_t* lut32 = reinterpret_cast<uint32_t*>(T.tab) + (size_t(t) << b);
-  // byte entries of fields 1..7: f | (slot - cum) << 8 | fp16(1024 + n) << 16 with
-  // n = 2 z + c - 2 dmin_f (the value relative to the field's smaller minimum)
-  const bool bywrite = T.byte_cand != 0 && field <= 7;
+  // byte entries: fields 1..7 as f | (slot - cum) << 8 | fp16(1024 + n) << 16 with
+  // n = 2 z + c - 2 dmin_f (the value relative to the field's smaller minimum), or
+  // every table as f | (slot - cum) << 8 | i16(2 z + c, or 4 m + c) << 16
+  const bool by16 = T.byte_cand == 2u;
+  const bool bywrite = (T.byte_cand == 1u && field <= 7) || by16;
   uint32_t* lutb = reinterpret_cast<uint32_t*>(T.tab + byte_off_of(b)) + (size_t(t) << b);
   const size_t lb = lut_bytes_of(tl, b);
   uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     for (uint32_t j = threadIdx.x; j < M; j += blockDim.x) {
       if (is_packed(tl)) {
         lut32[j] = 1u << 11;                          // f = 1, slot - cum = 0, symbol 0
-        if (bywrite) lutb[j] = 1u | (0x6400u << 16);  // f = 1, slot - cum = 0, n = 0
+        if (bywrite) lutb[j] = by16 ? 1u : 1u | (0x6400u << 16);  // f = 1, slot - cum = 0, value / n = 0
       } else if (tl == kTabNarrow) lut8[j] = 0;
       else lut16[j] = 0;
       if (split) {
@@ -337,9 +352,15 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
       }
       lut32[j] = (j - cum) | ((f & 0xFFFFu) << 11) | top;
       if (bywrite) {
-        const uint32_t n = uint32_t(2 * (int32_t(lo) + mn - T.dmin[field]) + int32_t(c));   // < 1024: checked on the host
         big8 |= f > 255u;
-        lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | ((0x6400u | n) << 16);
+        if (by16) {
+          const int32_t z = int32_t(lo) + mn;
+          const int32_t v = field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c);   // i16: checked on the host
+          lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | (uint32_t(uint16_t(int16_t(v))) << 16);
+        } else {
+          const uint32_t n = uint32_t(2 * (int32_t(lo) + mn - T.dmin[field]) + int32_t(c));   // < 1024: checked on the host
+          lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | ((0x6400u | n) << 16);
+        }
       }
     } else if (tl == kTabNarrow) {
       lut8[j] = uint8_t(lo);
@@ -491,9 +512,10 @@ __device__ __forceinline__ uint32_t add_f16x2(uint32_t a, uint32_t b) {
 // BT is the probability precision when known at compile time (0: read T.b),
 // TL the table layout (LDS tables start at LDS address 0), OK the output kind,
 // SP (hybrid layout) whether the per-slot entry maps are the ones staged in
-// LDS, CH the number of chains, BY (packed layout) whether fields 1..7 use the
-// byte entries.  `rings` points to this wave's 2*CH rings.
-template <int BT, int TL, int OK, bool SP, int CH, bool BY>
+// LDS, CH the number of chains, BY (packed and wide layouts) which byte entries
+// are staged: 0 none, 1 fields 1..7 in the fp16 form, 2 every table in the i16
+// form (DevTensor::byte_cand).  `rings` points to this wave's 2*CH rings.
+template <int BT, int TL, int OK, bool SP, int CH, int BY>
 __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0, uint32_t tile_end,
                                              const unsigned char* __restrict__ lds,
                                              uint16_t* __restrict__ rings) {
@@ -612,7 +634,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
   float kd[7] = {0, 0, 0, 0, 0, 0, 0}, k8d = 0.0f;
   int32_t m8d = 0;
   uint32_t kb[4] = {0, 0, 0, 0};
-  if (BY) {
+  if (BY == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) kb[i] = T.kbyte[i];
   }
@@ -748,7 +770,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           const uint32_t q = x[c] >> B;
-          if (BY && f <= 7) x[c] = add_byte1(e[c], mul_byte0(e[c], q));
+          if (BY == 2 || (BY == 1 && f <= 7)) x[c] = add_byte1(e[c], mul_byte0(e[c], q));
           else x[c] = __umul24(__builtin_amdgcn_ubfe(e[c], 11, fw), q) + (e[c] & 0x7FFu);
           ev[c][f] = e[c];
         }
@@ -766,7 +788,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
       }
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        if constexpr (BY) {
+        if constexpr (BY == 1) {
           // byte entries: the high halves hold fp16(1024 + 2 (z - dmin) + c);
           // pairs of them gathered by one permute and shifted by the fields'
           // constants 2 dmin - 1024 in one packed fp16 add are 2 z + c exactly,
@@ -797,6 +819,19 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
 #pragma unroll
             for (int i = 0; i < 7; ++i) yb[c][i] = __fmul_rn(yb[c][i], rv[c]);
           }
+        } else if constexpr (BY == 2) {
+          // i16 byte entries: the high half is the value 2 z + c (4 m + c for
+          // field 8, or 2 z8 + c), converted by one sign-extending select of
+          // the conversion; its bit 1 (bit 17 of the entry) is the parity of z,
+          // so the XOR over z1..z7 gives the parity of their sum, and
+          // 2 z8 + c = (4 m + c) + 2 par
+#pragma unroll
+          for (int f = 1; f <= 7; ++f) vv[c][f] = float(int32_t(ev[c][f]) >> 16);
+          const uint32_t x3 = __builtin_amdgcn_bitop3_b32(
+              __builtin_amdgcn_bitop3_b32(ev[c][1], ev[c][2], ev[c][3], 0x96),
+              __builtin_amdgcn_bitop3_b32(ev[c][4], ev[c][5], ev[c][6], 0x96), ev[c][7], 0x96);
+          par[c] = __builtin_amdgcn_ubfe(x3, 17, pw);
+          vv[c][8] = float((int32_t(ev[c][8]) >> 16) + int32_t(par[c] << 1));
         } else if (kDirectable && direct) {
           // direct entries: 0x4B400000 | (e >> 22) is the float 2^23 + 2^22 +
           // (2 z + c - 2 dmin), and one constant per field (the same for both
@@ -959,10 +994,10 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
         // slow rows: rv is g and 2 z + c is halved first (exactly)
         if (slow_rows) {
 #pragma unroll
-          for (int i = BY ? 8 : 1; i <= 8; ++i) v[i] = __fmul_rn(v[i], 0.5f);
+          for (int i = BY == 1 ? 8 : 1; i <= 8; ++i) v[i] = __fmul_rn(v[i], 0.5f);
         }
         float y[8];
-        if constexpr (BY) {
+        if constexpr (BY == 1) {
 #pragma unroll
           for (int i = 0; i < 7; ++i) y[i] = yb[c][i];
           y[7] = __fmul_rn(v[8], rv[c]);
@@ -1067,16 +1102,18 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     // hybrid layout: the per-slot entry maps when the build kept them, else the slot maps
     const bool split = has_split(TL, BT) && T.split != 0;
     // packed layout: the byte entries of fields 1..7 when the build kept them
-    constexpr bool kByteOk = TL == kTabPacked && OK != kOutLattice;
-    const bool bytev = kByteOk && T.bytev != 0;
+    // packed and wide layouts: the byte entries when the build kept them
+    constexpr bool kByteOk = (TL == kTabPacked || TL == kTabPackedWide) && OK != kOutLattice;
+    const uint32_t bmode = kByteOk && T.bytev != 0 ? T.byte_cand : 0u;
     if (TL != kTabWorkspace) {
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)(T.tab + (split ? split_off_of(BT) : 0));
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
       const uint32_t n16 = uint32_t((has_split(TL, BT) && !split ? lut_bytes_of(TL, BT) : kTab) / 16u);
-      if (kByteOk && bytev) {
-        // fields 1..7 from the byte tables, field 8 (same offset) from the packed ones
+      if (kByteOk && bmode != 0u) {
+        // the byte tables: fields 1..7 (field 8, at the same offset, from the
+        // packed ones), or all 16 tables
         const EP_GLOBAL u32x4* srcb = (const EP_GLOBAL u32x4*)(T.tab + byte_off_of(BT));
-        const uint32_t nb16 = uint32_t(byte_bytes_of(BT) / 16u);
+        const uint32_t nb16 = bmode == 1u ? uint32_t(byte_bytes_of(BT) / 16u) : n16;
         for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = i < nb16 ? srcb[i] : src[i];
       } else {
         for (uint32_t i = threadIdx.x; i < n16; i += kBlock) dst[i] = src[i];
@@ -1089,13 +1126,15 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     while (gr < ngroups) {
       if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
       if constexpr (has_split(TL, BT)) {
-        if (split) decode_tiles<BT, TL, OK, true, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        if (split) decode_tiles<BT, TL, OK, true, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       } else if constexpr (kByteOk) {
-        if (bytev) decode_tiles<BT, TL, OK, false, CH, true>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        if (bmode == 2u) decode_tiles<BT, TL, OK, false, CH, 2>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else if (TL == kTabPacked && bmode == 1u)
+          decode_tiles<BT, TL, OK, false, CH, (TL == kTabPacked ? 1 : 0)>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        else decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       } else {
-        decode_tiles<BT, TL, OK, false, CH, false>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
+        decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
       }
       gr = __builtin_amdgcn_readfirstlane(nx);
     }
@@ -1237,6 +1276,25 @@ bool byte_candidate(const ep_tensor_desc& d, uint32_t variant) {
   return true;
 }
 
+// Which byte entries a tensor gets (the table build still checks every f < 256
+// of the tables it writes and drops them otherwise): 1 (fields 1..7, fp16 form)
+// for the candidates above; 2 (all 16 tables, i16 form) for any other packed or
+// wide tensor whose values 2 z + c and 4 m + c (2 z8 + c) all fit 16 bits.
+uint32_t byte_mode(const ep_tensor_desc& d, uint32_t variant) {
+  if (byte_candidate(d, variant)) return 1;
+  const int tl = layout_of(variant);
+  if (tl != kTabPacked && tl != kTabPackedWide) return 0;
+  const int64_t k8 = d.field8 == EP_FIELD8_Z8 ? 2 : 4;
+  for (int k = 1; k < kTables; ++k) {
+    if (d.alphabet[k] == 0) continue;
+    const int64_t mul = k >= 15 ? k8 : 2, c = (k - 1) & 1;
+    const int64_t lo = mul * int64_t(d.min_offset[k]) + c;
+    const int64_t hi = mul * (int64_t(d.min_offset[k]) + d.alphabet[k] - 1) + c;
+    if (lo < -32768 || hi > 32767) return 0;
+  }
+  return 2;
+}
+
 // IEEE binary16 bits of an integer v, |v| <= 2048 (exactly representable)
 uint32_t f16_bits_of_int(int32_t v) {
   if (v == 0) return 0;
@@ -1269,8 +1327,9 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
     L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
     L.tab_bytes[i] = storage_bytes_of(layout_of(L.variant[i]), d.prob_bits);
-    L.byte_cand[i] = byte_candidate(d, L.variant[i]) ? 1 : 0;
-    if (L.byte_cand[i]) L.tab_bytes[i] += byte_bytes_of(d.prob_bits);
+    L.byte_cand[i] = char(byte_mode(d, L.variant[i]));
+    if (L.byte_cand[i] == 1) L.tab_bytes[i] += byte_bytes_of(d.prob_bits);
+    if (L.byte_cand[i] == 2) L.tab_bytes[i] += byte16_bytes_of(d.prob_bits);
     L.max_chunks += (d.num_tiles + 1) / 2;
     L.group_tiles[L.group[i]] += d.num_tiles;
   }
@@ -1533,10 +1592,10 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       D.kvals[26] = uint32_t(d.field8 == EP_FIELD8_Z8 ? 0 : (kd8 ? -2 : 2));
       D.direct = direct ? 1u : 0u;
       // byte entries: the fp16 constants 2 dmin_f - 1024 of fields 1..7, in pairs
-      D.byte_cand = L.byte_cand[i] ? 1u : 0u;
-      D.bytev = D.byte_cand;
+      D.byte_cand = uint32_t(L.byte_cand[i]);
+      D.bytev = D.byte_cand != 0u ? 1u : 0u;
       uint32_t kh[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (D.byte_cand)
+      if (D.byte_cand == 1u)
         for (int f = 1; f <= 7; ++f) kh[f] = f16_bits_of_int(2 * D.dmin[f] - 1024);   // in [-2048, 0]
       D.kbyte[0] = kh[1] | (kh[2] << 16);
       D.kbyte[1] = kh[3] | (kh[4] << 16);
