@@ -1064,6 +1064,25 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
   }
 }
 
+// One unit of work: the 2*CH tiles from tile0 with the entry form the build kept.
+template <int BT, int TL, int OK, int CH>
+__device__ __forceinline__ void decode_group(const DevTensor& T, uint32_t tile0, uint32_t t_end,
+                                             const unsigned char* __restrict__ smem,
+                                             uint16_t* __restrict__ rings, bool split, uint32_t bmode) {
+  constexpr bool kByteOk = (TL == kTabPacked || TL == kTabPackedWide) && OK != kOutLattice;
+  if constexpr (has_split(TL, BT)) {
+    if (split) decode_tiles<BT, TL, OK, true, CH, 0>(T, tile0, t_end, smem, rings);
+    else decode_tiles<BT, TL, OK, false, CH, 0>(T, tile0, t_end, smem, rings);
+  } else if constexpr (kByteOk) {
+    if (bmode == 2u) decode_tiles<BT, TL, OK, false, CH, 2>(T, tile0, t_end, smem, rings);
+    else if (TL == kTabPacked && bmode == 1u)
+      decode_tiles<BT, TL, OK, false, CH, (TL == kTabPacked ? 1 : 0)>(T, tile0, t_end, smem, rings);
+    else decode_tiles<BT, TL, OK, false, CH, 0>(T, tile0, t_end, smem, rings);
+  } else {
+    decode_tiles<BT, TL, OK, false, CH, 0>(T, tile0, t_end, smem, rings);
+  }
+}
+
 // Persistent decode kernel.  Block i owns a contiguous range of chunks (up to
 // tiles_per_chunk tiles of one tensor each), which splits into runs of chunks
 // from the same tensor.  For each run the block stages the tensor's decode
@@ -1120,22 +1139,25 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
       }
     }
     __syncthreads();
-    // the first group of each wave is its own index, which spreads a short run
-    // over the SIMDs (wave w runs on SIMD w mod 4); later groups come from the counter
+    // Units of work: groups of kGroup tiles, except that a run's last partial
+    // round, when it holds at most half as many groups as the block has waves,
+    // is split into tile pairs run as one chain each, so that twice as many
+    // waves share it (a run ends at a block barrier, so its last round sets the
+    // run's time).  The first unit of each wave is its own index, which spreads
+    // a short run over the SIMDs (wave w runs on SIMD w mod 4); later units come
+    // from the counter.
+    uint32_t u4 = ngroups;
+    if constexpr (CH > 1) {
+      const uint32_t r = ngroups % uint32_t(kWavesPerBlock);
+      if (r != 0u && r <= uint32_t(kWavesPerBlock) / 2u) u4 = ngroups - r;
+    }
+    const uint32_t t4 = ch.tile0 + kGroup * u4;              // first tile of the pairs
+    const uint32_t nunits = u4 + (t_end > t4 ? (t_end - t4 + 1u) / 2u : 0u);
     uint32_t gr = threadIdx.x >> 6, nx = 0;
-    while (gr < ngroups) {
+    while (gr < nunits) {
       if (lane0) nx = kWavesPerBlock + atomicAdd(ctr + ci, 1u);
-      if constexpr (has_split(TL, BT)) {
-        if (split) decode_tiles<BT, TL, OK, true, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-      } else if constexpr (kByteOk) {
-        if (bmode == 2u) decode_tiles<BT, TL, OK, false, CH, 2>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else if (TL == kTabPacked && bmode == 1u)
-          decode_tiles<BT, TL, OK, false, CH, (TL == kTabPacked ? 1 : 0)>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-        else decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-      } else {
-        decode_tiles<BT, TL, OK, false, CH, 0>(T, ch.tile0 + kGroup * gr, t_end, smem, rings);
-      }
+      if (CH == 1 || gr < u4) decode_group<BT, TL, OK, CH>(T, ch.tile0 + kGroup * gr, t_end, smem, rings, split, bmode);
+      else decode_group<BT, TL, OK, 1>(T, t4 + 2u * (gr - u4), t_end, smem, rings, split, bmode);
       gr = __builtin_amdgcn_readfirstlane(nx);
     }
     ci = cn;
