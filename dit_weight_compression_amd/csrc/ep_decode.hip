@@ -1102,9 +1102,10 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
   constexpr size_t kTab = lds_table_bytes_of(TL, BT);
   constexpr uint32_t kGroup = 2u * CH;                     // tiles per wave group
   __shared__ __align__(16) unsigned char smem[kTab + ring_bytes_of(CH)];
-  const uint32_t per = (nchunks + gridDim.x - 1) / gridDim.x;
-  const uint32_t c0 = blockIdx.x * per;
-  const uint32_t c1 = min(nchunks, c0 + per);
+  // an even share of the chunks per block (chunks are one group of tiles, so
+  // the blocks' shares differ by at most one group)
+  const uint32_t c0 = uint32_t((uint64_t(blockIdx.x) * nchunks) / gridDim.x);
+  const uint32_t c1 = uint32_t((uint64_t(blockIdx.x + 1u) * nchunks) / gridDim.x);
   const bool lane0 = (threadIdx.x & 63u) == 0;
   // LDS: [decode tables (LDS layouts)][2 * CH rings of kRingWords per wave]
   uint16_t* rings = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 6) * (kGroup * kRingWords);
@@ -1445,17 +1446,11 @@ uint32_t chains_for(size_t tiles, uint32_t resident) {
   return tiles >= size_t(4) * 2 * kMaxChains * kWavesPerBlock * resident ? 2u : 1u;
 }
 
-// Tiles per chunk: full blocks (2 * chains tiles per wave) when there is enough
-// work to fill every resident block many times over; otherwise spread the
-// tiles over all resident blocks (even counts, one tile per half-wave), since a
-// tile is a sequential unit and a small batch is bound by the per-tile decode
-// latency.
-uint32_t tiles_per_chunk(size_t tiles, uint32_t resident, uint32_t chains) {
-  const uint32_t full = 2u * chains * kWavesPerBlock;
-  if (tiles >= size_t(full) * resident) return full;
-  const size_t per = (tiles + 2 * size_t(resident) - 1) / (2 * size_t(resident));
-  return uint32_t(std::min<size_t>(full, std::max<size_t>(2, 2 * per)));
-}
+// Tiles per chunk: one group (2 * chains tiles, the unit a wave decodes), so
+// that the blocks' even shares of the chunks differ by at most one group.  A
+// block's consecutive chunks of one tensor form one run; a small batch spreads
+// over every resident block.
+uint32_t tiles_per_chunk(uint32_t chains) { return 2u * chains; }
 
 }  // namespace
 
@@ -1527,7 +1522,7 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       rc = resident_grid(v, G.chains, &resident);
       if (rc != EP_OK) return rc;
     }
-    G.tiles_per_chunk = tiles_per_chunk(L.group_tiles[v], resident, G.chains);
+    G.tiles_per_chunk = tiles_per_chunk(G.chains);
     for (int i = 0; i < n; ++i)
       if (L.group[i] == v) group_chunks[v] += (descs[i].num_tiles + G.tiles_per_chunk - 1) / G.tiles_per_chunk;
     G.grid = uint32_t(std::min<size_t>(resident, group_chunks[v]));
