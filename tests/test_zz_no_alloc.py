@@ -68,8 +68,9 @@ def test_two_calls_in_a_row_match_the_workspace_entry_point():
 
 def test_batch_beyond_the_scratch_is_rejected_before_any_work():
     one = _packed([(512, 1024, 4.0, "direct", 32)])[0]
-    need = ep.workspace_size([one])
-    n = ep.NOALLOC_SCRATCH_BYTES // need + 2
+    base = ep.workspace_size([one])
+    per = ep.workspace_size([one, one]) - base          # what each further tensor adds
+    n = (ep.NOALLOC_SCRATCH_BYTES - base) // per + 3
     packed = [one] * n
     assert ep.workspace_size(packed) > ep.NOALLOC_SCRATCH_BYTES
     outs = [torch.zeros((one.rows, one.cols), dtype=torch.int16, device="cuda") for _ in range(n)]
