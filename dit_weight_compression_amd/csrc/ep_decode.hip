@@ -207,10 +207,13 @@ __device__ __forceinline__ uint32_t block_scan256_excl(uint32_t v, uint32_t* __r
   return kMax ? max(pre, ex) : pre + ex;
 }
 
-// Dynamic LDS of the table build: the slot marks (M u16) and the table's
-// frequencies (A u16) of the largest table in the batch.
-constexpr size_t build_lds_bytes(uint32_t max_b, uint32_t max_alphabet) {
-  return ((size_t(2) << max_b) + 2u * size_t(max_alphabet) + 15u) / 16u * 16u;
+// Dynamic LDS of the table build for one tensor's tables: packed layouts
+// first stage their entries (two u32 per slot: packed and byte entries) so
+// that the copy to the workspace is coalesced; then the slot marks (u16 per
+// slot) and the table's frequencies (u16 per symbol).  The launch takes the
+// largest over the batch.
+__host__ __device__ constexpr size_t build_lds_bytes(bool packed, uint32_t b, uint32_t alphabet) {
+  return (packed ? size_t(8) << b : 0) + (((size_t(2) << b) + 2u * size_t(alphabet) + 15u) / 16u * 16u);
 }
 
 // One block per (coordinate table, tensor): cumulative frequencies by a block
@@ -274,9 +277,12 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   const size_t lb = lut_bytes_of(tl, b);
   uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
   float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
-  extern __shared__ uint16_t build_lds[];
-  uint16_t* mark = build_lds;                  // per slot: 1 + the symbol whose interval starts there, else 0
-  uint16_t* fl = build_lds + M;                // the table's frequencies
+  extern __shared__ __align__(16) uint32_t build_lds[];
+  uint32_t* st32 = build_lds;                  // packed layouts: staged entries, packed then byte
+  uint32_t* stb = build_lds + M;
+  uint16_t* mark = reinterpret_cast<uint16_t*>(build_lds + (is_packed(tl) ? 2u * M : 0u));
+  uint16_t* fl = mark + M;                     // the table's frequencies
+  // per slot, mark: 1 + the symbol whose interval starts there, else 0
   __shared__ uint32_t part[4];
   if (!is_packed(tl)) {
     for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
@@ -350,16 +356,16 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         const int32_t d = int32_t(lo) + mn - T.dmin[field];
         top = uint32_t((field < 8 || T.f8z8 ? 2 * d : 4 * d) + int32_t(c)) << 22;
       }
-      lut32[j] = (j - cum) | ((f & 0xFFFFu) << 11) | top;
+      st32[j] = (j - cum) | ((f & 0xFFFFu) << 11) | top;
       if (bywrite) {
         big8 |= f > 255u;
         if (by16) {
           const int32_t z = int32_t(lo) + mn;
           const int32_t v = field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c);   // i16: checked on the host
-          lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | (uint32_t(uint16_t(int16_t(v))) << 16);
+          stb[j] = (f & 0xFFu) | ((j - cum) << 8) | (uint32_t(uint16_t(int16_t(v))) << 16);
         } else {
           const uint32_t n = uint32_t(2 * (int32_t(lo) + mn - T.dmin[field]) + int32_t(c));   // < 1024: checked on the host
-          lutb[j] = (f & 0xFFu) | ((j - cum) << 8) | ((0x6400u | n) << 16);
+          stb[j] = (f & 0xFFu) | ((j - cum) << 8) | ((0x6400u | n) << 16);
         }
       }
     } else if (tl == kTabNarrow) {
@@ -375,6 +381,14 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         // |value| < 2^15: checked on the host
         sval[j] = int16_t(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
       }
+    }
+  }
+  if (is_packed(tl)) {
+    // the staged entries to the workspace, 16 bytes per thread and store
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < M / 4u; i += blockDim.x) {
+      reinterpret_cast<u32x4*>(lut32)[i] = reinterpret_cast<const u32x4*>(st32)[i];
+      if (bywrite) reinterpret_cast<u32x4*>(lutb)[i] = reinterpret_cast<const u32x4*>(stb)[i];
     }
   }
   // per-slot entries hold f in 7 bits: any larger frequency disables them for the tensor
@@ -1651,14 +1665,15 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     uint64_t max_rows = 1;
     for (int i = 0; i < n; ++i) max_rows = std::max<uint64_t>(max_rows, uint64_t(descs[i].rows));
     const uint32_t row_blocks = uint32_t((max_rows + 1023) / 1024);
-    uint32_t max_b = 9, max_a = 0;
+    size_t lds_bytes = 16;
     for (int i = 0; i < n; ++i) {
       if (descs[i].num_tiles == 0) continue;
-      max_b = std::max(max_b, descs[i].prob_bits);
-      for (int k = 1; k < kTables; ++k) max_a = std::max(max_a, descs[i].alphabet[k]);
+      uint32_t amax = 0;
+      for (int k = 1; k < kTables; ++k) amax = std::max(amax, descs[i].alphabet[k]);
+      lds_bytes = std::max(lds_bytes, build_lds_bytes(is_packed(layout_of(L.variant[i])), descs[i].prob_bits, amax));
     }
     hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks + chunk_blocks, n), dim3(256),
-                       uint32_t(build_lds_bytes(max_b, max_a)), st,
+                       uint32_t(lds_bytes), st,
                        reinterpret_cast<DevTensor*>(wsb + L.tens_off), reinterpret_cast<Chunk*>(wsb + L.chunk_off),
                        row_blocks);
     e = hipGetLastError();
