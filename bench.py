@@ -347,11 +347,18 @@ def calibrate_copy(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def _time_ms(fn, reps: int, warmup: int = 3) -> float:
+def _time_ms(fn, reps: int, warmup: int = 3, warm_s: float = 0.2) -> float:
+    """Mean time of fn over reps calls, after at least `warmup` calls and warm_s
+    seconds of untimed calls (the GPU clock ramps for tens of milliseconds after
+    host-side work such as encoding, longer than a few short launches take)."""
     import torch
 
-    for _ in range(warmup):
+    t0, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0 < warm_s:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -643,7 +650,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--max-tensors", type=int, default=0, help="use only the first N tensors")
     ap.add_argument("--threads", type=int, default=default_threads(),

@@ -1155,16 +1155,22 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     }
     __syncthreads();
     // Units of work: groups of kGroup tiles, except that a run's last partial
-    // round, when it holds at most half as many groups as the block has waves,
-    // is split into tile pairs run as one chain each, so that twice as many
-    // waves share it (a run ends at a block barrier, so its last round sets the
-    // run's time).  The first unit of each wave is its own index, which spreads
-    // a short run over the SIMDs (wave w runs on SIMD w mod 4); later units come
-    // from the counter.
+    // round is split into tile pairs run as one chain each, so that more waves
+    // share it (a run ends at a block barrier, so its last round sets the run's
+    // time).  With every table in LDS a round is bound by VALU issue, which the
+    // partial round leaves spare: one-chain pairs finish sooner even where some
+    // waves take two of them in turn.  Where the tables are read through the
+    // caches (hybrid and workspace layouts) a round waits on those reads and a
+    // wave's two chains hide each other's waits, so the split is taken only when
+    // the pairs need no more than one round (at most half as many groups as the
+    // block has waves).  The first unit of each wave is its own index, which
+    // spreads a short run over the SIMDs (wave w runs on SIMD w mod 4); later
+    // units come from the counter.
     uint32_t u4 = ngroups;
     if constexpr (CH > 1) {
+      constexpr bool kLdsTables = storage_of(TL) != kTabWorkspace;
       const uint32_t r = ngroups % uint32_t(kWavesPerBlock);
-      if (r != 0u && r <= uint32_t(kWavesPerBlock) / 2u) u4 = ngroups - r;
+      if (r != 0u && (kLdsTables || r <= uint32_t(kWavesPerBlock) / 2u)) u4 = ngroups - r;
     }
     const uint32_t t4 = ch.tile0 + kGroup * u4;              // first tile of the pairs
     const uint32_t nunits = u4 + (t_end > t4 ? (t_end - t4 + 1u) / 2u : 0u);
