@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
@@ -128,16 +130,16 @@ struct alignas(16) DevTensor {
   uint32_t tab_bytes;        // bytes of the table block
   uint32_t payload_bytes;    // readable payload bytes: words rounded up to 8, times 2
   uint32_t out_bytes;        // output bytes (every tile's stores stay below this)
-  uint32_t slow_rows;        // set by the table build when some row's g/2 is inexact: use g
+  uint32_t call;             // the preparing call's number (never 0); a bad_* word holding it is set
   uint32_t f8z8;             // 1: field 8 holds z8 (no parity reduction), 0: it holds m
   uint32_t chunk0;           // index of the tensor's first chunk in the schedule
   uint32_t tpc;              // tiles per chunk of the tensor's launch group
   uint32_t direct;           // packed layouts: entries hold the value 2 z + c - 2 dmin (see kvals)
-  uint32_t split;            // hybrid layout: 1 = per-slot entries usable (cleared by the build if some f > 127)
+  uint32_t split;            // hybrid layout: 1 = per-slot entries usable, unless bad_split says otherwise
   uint32_t byte_cand;        // byte-entry tables in the workspace (set by the host): 0 none; 1 fields 1..7 as
                              // f | (slot - cum) << 8 | fp16(1024 + 2 (z - dmin) + c) << 16 (direct packed
                              // tensors); 2 all 16 tables as f | (slot - cum) << 8 | i16 value << 16
-  uint32_t bytev;            // ... and they are usable (cleared by the build if some f > 255)
+  uint32_t bytev;            // ... and they are usable, unless bad_bytes says otherwise
   uint32_t kbyte[4];         // byte entries: fp16 pairs (2 dmin_f - 1024) for fields (1,2), (3,4), (5,6), (-,7)
   int32_t dmin[9];           // direct entries: per field, the smaller of the two cosets' minima
   uint64_t payload_words;
@@ -161,14 +163,23 @@ struct alignas(16) DevTensor {
   int32_t minv[kTables];
   uint32_t freq_base[kTables];
   uint32_t alphabet[kTables];
+  // Flags that depend on device data, stored by the table build's blocks as
+  // the call number when the condition holds (never written otherwise, so no
+  // word has to be cleared first; a stale or unrelated value that happens to
+  // equal the number only selects the slower exact path):
+  uint32_t bad_split;        // a table of the hybrid layout has f > 127: the per-slot entries are unusable
+  uint32_t bad_bytes;        // a byte-entry table has f > 255: the byte entries are unusable
+  uint32_t bad_rows;         // some row's g / 2 is inexact: multiply by g
 };
 
 // The layout checks in the tests read these fields of the workspace copy
 // (descriptor i at byte i * sizeof(DevTensor)) back after ep_batch_prepare.
-static_assert(sizeof(DevTensor) == 560, "DevTensor layout read by the tests");
-static_assert(offsetof(DevTensor, variant) == 36 && offsetof(DevTensor, slow_rows) == 56 &&
+static_assert(sizeof(DevTensor) == 576, "DevTensor layout read by the tests");
+static_assert(offsetof(DevTensor, variant) == 36 && offsetof(DevTensor, call) == 56 &&
                   offsetof(DevTensor, direct) == 72 && offsetof(DevTensor, split) == 76 &&
-                  offsetof(DevTensor, byte_cand) == 80 && offsetof(DevTensor, bytev) == 84,
+                  offsetof(DevTensor, byte_cand) == 80 && offsetof(DevTensor, bytev) == 84 &&
+                  offsetof(DevTensor, bad_split) == 556 && offsetof(DevTensor, bad_bytes) == 560 &&
+                  offsetof(DevTensor, bad_rows) == 564,
               "DevTensor layout read by the tests");
 
 struct Chunk {
@@ -177,6 +188,17 @@ struct Chunk {
 };
 
 thread_local std::string g_last_error;
+
+// A number per ep_batch_prepare call, never 0, starting from a clock-derived
+// value so that numbers left in reused memory by another process rarely match.
+uint32_t next_call_number() {
+  static std::atomic<uint32_t> counter{
+      uint32_t(std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B1ull) | 1u};
+  uint32_t v;
+  do v = counter.fetch_add(1u, std::memory_order_relaxed);
+  while (v == 0u);
+  return v;
+}
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
@@ -216,13 +238,45 @@ __host__ __device__ constexpr size_t build_lds_bytes(bool packed, uint32_t b, ui
   return (packed ? size_t(8) << b : 0) + (((size_t(2) << b) + 2u * size_t(alphabet) + 15u) / 16u * 16u);
 }
 
-// One block per (coordinate table, tensor): cumulative frequencies by a block
-// scan over per-thread symbol ranges; every symbol with f > 0 marks the slot
-// where its interval starts, and a forward scan over the slots carries the
-// last mark, which is the slot's symbol (a zero-frequency symbol never marks).
+// Batches of up to kArgTensors tensors pass their descriptors to the table
+// build as kernel arguments (576 bytes each; the argument block stays under
+// 4 KiB), so no host-to-device copy precedes the build, and one more block per
+// tensor writes the descriptor to the workspace; larger batches copy the
+// descriptors to the workspace before the build.
+constexpr int kArgTensors = 6;
+template <int NA>
+struct DescArgs {
+  DevTensor t[NA];
+};
+template <>
+struct DescArgs<0> {};
+
+// Per tensor (blockIdx.y): 16 table blocks, row_blocks blocks of row
+// multipliers, the blocks of its tile schedule and, with descriptors in the
+// kernel arguments, the block that writes the descriptor.
+//
+// A table block: cumulative frequencies by a block scan over per-thread symbol
+// ranges; every symbol with f > 0 marks the slot where its interval starts, and
+// a forward scan over the slots carries the last mark, which is the slot's
+// symbol (a zero-frequency symbol never marks).
+template <int NA>
 __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict__ tens, Chunk* __restrict__ chunks,
-                                                          uint32_t row_blocks) {
-  DevTensor& T = tens[blockIdx.y];
+                                                          uint32_t row_blocks, DescArgs<NA> args) {
+  const DevTensor& T = [&]() -> const DevTensor& {
+    if constexpr (NA > 0) return args.t[blockIdx.y];
+    else return tens[blockIdx.y];
+  }();
+  DevTensor& W = tens[blockIdx.y];             // the workspace copy: flags are stored there
+  if constexpr (NA > 0) {
+    if (blockIdx.x == gridDim.x - 1u) {
+      // every word up to the flags, which only the blocks that find a condition write
+      constexpr uint32_t kWords = offsetof(DevTensor, bad_split) / 4u;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(&T);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&W);
+      for (uint32_t i = threadIdx.x; i < kWords; i += blockDim.x) dst[i] = src[i];
+      return;
+    }
+  }
   if (T.T == 0) return;
   if (blockIdx.x >= 16 + row_blocks) {
     // the tensor's entries of the tile schedule, 1024 per block
@@ -250,7 +304,7 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
         T.rowv[T.rows + r] = gr;
       }
     }
-    if (inexact) atomicOr(&T.slow_rows, 1u);
+    if (__syncthreads_or(inexact) && threadIdx.x == 0) W.bad_rows = T.call;
     return;
   }
   const uint32_t k = 1 + blockIdx.x;            // table index 1..16
@@ -392,9 +446,9 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
     }
   }
   // per-slot entries hold f in 7 bits: any larger frequency disables them for the tensor
-  if (__syncthreads_or(big) && threadIdx.x == 0) atomicAnd(&T.split, 0u);
+  if (__syncthreads_or(big) && threadIdx.x == 0) W.bad_split = T.call;
   // byte entries hold f in 8 bits: any larger frequency disables them for the tensor
-  if (__syncthreads_or(big8) && threadIdx.x == 0) atomicAnd(&T.bytev, 0u);
+  if (__syncthreads_or(big8) && threadIdx.x == 0) W.bad_bytes = T.call;
 }
 
 // ---------------------------------------------------------------- container rounding
@@ -555,7 +609,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
   const uint32_t payload_bytes = T.payload_bytes;
   const __amdgpu_buffer_rsrc_t rO = make_rsrc(T.out, out_bytes);
   const __amdgpu_buffer_rsrc_t rR = make_rsrc(T.rowv, T.rows * 8u);
-  const bool slow_rows = T.slow_rows != 0;
+  const bool slow_rows = T.bad_rows == T.call;
 
   // ---- per-chain tile start.  Uniform values of a chain's two tiles live in
   // scalar registers; each lane keeps its half's ring read pointer (vP) so
@@ -1134,11 +1188,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
     __syncthreads();                       // every wave is done with the previous run
     if (threadIdx.x == 0) __hip_atomic_store(ctr + ci, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // hybrid layout: the per-slot entry maps when the build kept them, else the slot maps
-    const bool split = has_split(TL, BT) && T.split != 0;
+    const bool split = has_split(TL, BT) && T.split != 0 && T.bad_split != T.call;
     // packed layout: the byte entries of fields 1..7 when the build kept them
     // packed and wide layouts: the byte entries when the build kept them
     constexpr bool kByteOk = (TL == kTabPacked || TL == kTabPackedWide) && OK != kOutLattice;
-    const uint32_t bmode = kByteOk && T.bytev != 0 ? T.byte_cand : 0u;
+    const uint32_t bmode = kByteOk && T.bytev != 0 && T.bad_bytes != T.call ? T.byte_cand : 0u;
     if (TL != kTabWorkspace) {
       const EP_GLOBAL u32x4* src = (const EP_GLOBAL u32x4*)(T.tab + (split ? split_off_of(BT) : 0));
       u32x4* dst = reinterpret_cast<u32x4*>(smem);
@@ -1519,8 +1573,10 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
-  // only the descriptors travel; the build kernel writes the tile schedule
+  // only the descriptors travel (for small batches as the table build's kernel
+  // arguments); the build kernel writes the tile schedule
   std::vector<unsigned char> host(L.chunk_off, 0);
+  const uint32_t call = next_call_number();
   DevTensor* ht = reinterpret_cast<DevTensor*>(host.data() + L.tens_off);
   uint32_t chunk_blocks = 0;
   char* wsb = static_cast<char*>(workspace);
@@ -1581,7 +1637,8 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     D.freqs = d.freqs;
     D.tab = reinterpret_cast<unsigned char*>(wsb + L.tab_off[i]);
     D.rowv = reinterpret_cast<float*>(wsb + L.row_off[i]);
-    D.slow_rows = 0;
+    D.call = call;
+    D.bad_split = D.bad_bytes = D.bad_rows = 0;
     D.f8z8 = d.field8 == EP_FIELD8_Z8 ? 1u : 0u;
     D.out = outs[i];
     D.status = tile_status ? tile_status[i] : nullptr;
@@ -1664,9 +1721,12 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
     chunk_blocks = std::max<uint32_t>(chunk_blocks, (nch + 1023u) / 1024u);
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = host.empty() ? hipSuccess
-                              : hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+  hipError_t e = hipSuccess;
+  const bool by_args = n <= kArgTensors;
+  if (n > 0 && !by_args) {
+    e = hipMemcpyAsync(wsb, host.data(), host.size(), hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(e));
+  }
   if (n > 0) {
     uint64_t max_rows = 1;
     for (int i = 0; i < n; ++i) max_rows = std::max<uint64_t>(max_rows, uint64_t(descs[i].rows));
@@ -1678,10 +1738,18 @@ int ep_batch_prepare(const ep_tensor_desc* descs, const int* dtypes, void* const
       for (int k = 1; k < kTables; ++k) amax = std::max(amax, descs[i].alphabet[k]);
       lds_bytes = std::max(lds_bytes, build_lds_bytes(is_packed(layout_of(L.variant[i])), descs[i].prob_bits, amax));
     }
-    hipLaunchKernelGGL(build_tables_kernel, dim3(16 + row_blocks + chunk_blocks, n), dim3(256),
-                       uint32_t(lds_bytes), st,
-                       reinterpret_cast<DevTensor*>(wsb + L.tens_off), reinterpret_cast<Chunk*>(wsb + L.chunk_off),
-                       row_blocks);
+    DevTensor* tens = reinterpret_cast<DevTensor*>(wsb + L.tens_off);
+    Chunk* chunks = reinterpret_cast<Chunk*>(wsb + L.chunk_off);
+    if (by_args) {
+      DescArgs<kArgTensors> a;
+      std::memset(&a, 0, sizeof(a));
+      std::memcpy(a.t, ht, sizeof(DevTensor) * size_t(n));
+      hipLaunchKernelGGL(build_tables_kernel<kArgTensors>, dim3(16 + row_blocks + chunk_blocks + 1, n), dim3(256),
+                         uint32_t(lds_bytes), st, tens, chunks, row_blocks, a);
+    } else {
+      hipLaunchKernelGGL(build_tables_kernel<0>, dim3(16 + row_blocks + chunk_blocks, n), dim3(256),
+                         uint32_t(lds_bytes), st, tens, chunks, row_blocks, DescArgs<0>{});
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return fail(EP_ERR_HIP, std::string("table build launch: ") + hipGetErrorString(e));
   }

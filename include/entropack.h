@@ -167,10 +167,16 @@ int ep_decode_tensor(const ep_tensor_desc* desc, int dtype, void* out, int32_t* 
  *   are rejected with EP_ERR_WORKSPACE before any GPU work (split them, or use
  *   ep_decode_batch).
  *   Sharing: all calls on one GPU use that GPU's one array, which keeps the
- *   last call's contents; every byte a call reads there it has written first.
+ *   last call's contents; every byte a call reads there it has written first,
+ *   except three flag words per tensor, which choose between exact decode
+ *   paths (a leftover value can at worst choose the slower one).
  *   Calls that overlap on one GPU (on different streams, or from host threads
  *   without ordering) race on the array and give undefined results: order
  *   them on one stream.
+ *   Stream capture: a batch of at most 6 tensors records only kernel launches
+ *   (its descriptors travel as kernel arguments); a larger batch also records
+ *   a copy from a host buffer that lives only for the call, so a graph that
+ *   holds one must not be replayed.
  * Other arguments, errors and tile statuses: as ep_decode_batch.
  */
 #define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
@@ -180,8 +186,10 @@ int ep_decode_batch_noalloc(const ep_tensor_desc* descs, const int* dtypes, void
 /*
  * The two halves of ep_decode_batch, for callers that time the decode kernel
  * on its own.  ep_batch_prepare validates the arguments and enqueues the
- * upload of the schedule and the decode-table build; ep_batch_launch enqueues
- * the fused decode kernel.  `plan` is caller-owned host memory filled by
+ * build of the decode tables and the tile schedule (for a batch of at most 6
+ * tensors the descriptors are that kernel's arguments; a larger batch copies
+ * them to the workspace first); ep_batch_launch enqueues the fused decode
+ * kernel.  `plan` is caller-owned host memory filled by
  * prepare; launch must follow its prepare on the same stream with the same
  * workspace.
  */

@@ -8,8 +8,9 @@ entries of all tables (other packed and wide tensors), both needing every
 f < 256.  The decoded weights are identical whichever form runs, so parity
 alone cannot show which one did.  These tests read the descriptor the library
 wrote to the workspace after ep_batch_prepare (its field offsets are pinned by
-static_asserts in the decoder source), check the expected form, then compare
-the decode with the oracle.
+static_asserts in the decoder source): the host's choice, and the table build's
+flags, which hold the call's number when a frequency rules a form out.  They
+check the expected form, then compare the decode with the oracle.
 
 Inputs are oracle-encoded seeded weights; some containers get a table's
 min_offset shifted, which keeps the coded symbols valid and moves the decoded
@@ -30,8 +31,9 @@ pytestmark = pytest.mark.gpu
 
 ep = pytest.importorskip("dit_weight_compression_amd")
 
-DEVTENSOR_BYTES = 560
-FIELD_OFFSET = {"variant": 36, "direct": 72, "split": 76, "byte_cand": 80, "bytev": 84}
+DEVTENSOR_BYTES = 576
+FIELD_OFFSET = {"variant": 36, "call": 56, "direct": 72, "split": 76, "byte_cand": 80, "bytev": 84,
+                "bad_split": 556, "bad_bytes": 560}
 P11, W11, H11 = 2, 4, 6          # decode-table placements (the library's Variant numbering)
 
 
@@ -61,7 +63,12 @@ def _read_flags(ct):
     batch.prepare(ep.C.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     rec = ws[:DEVTENSOR_BYTES].cpu().numpy().view(np.uint32)
-    return {name: int(rec[off // 4]) for name, off in FIELD_OFFSET.items()}
+    raw = {name: int(rec[off // 4]) for name, off in FIELD_OFFSET.items()}
+    assert raw["call"] != 0
+    # the form the decoder runs: the host's choice unless the build ruled it out
+    raw["split"] = int(raw["split"] != 0 and raw["bad_split"] != raw["call"])
+    raw["bytev"] = int(raw["bytev"] != 0 and raw["bad_bytes"] != raw["call"])
+    return raw
 
 
 def _parity(ct, kinds, label):
