@@ -798,6 +798,9 @@ def main():
             "tiles_ok": tiles_ok,
             "weight_error_pct": rel_l2,
             "copy_gbs_measured": None,
+            # roofline.traffic is not counted in this run: it is the committed rocprofv3
+            # FETCH_SIZE + WRITE_SIZE record for this kernel source and workload (or null)
+            "traffic_source": None,
         },
         "roofline": {
             "bound": "hbm",
@@ -808,6 +811,9 @@ def main():
             "traffic": measured_traffic(args.workload, len(packed)),
         },
     }
+    if result["roofline"]["traffic"] is not None:
+        result["config"]["traffic_source"] = (os.path.relpath(TRAFFIC_RECORD, ROOT) +
+                                              " (rocprofv3 counter record of this kernel source, copy-scaled)")
     log(f"[bench] {len(packed)} tensors, {numel / 1e9:.3f} G weights, {8 * stored / numel:.4f} bpp; "
         f"step {ms:.3f} ms, kernel {kms:.3f} ms, wall {t_wall * 1e3 / args.steps:.3f} ms/step")
     del outs, batch, ws
