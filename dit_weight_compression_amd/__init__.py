@@ -76,6 +76,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                               "(there is no CPU fallback for the decoder)")
+        # torch first: it loads the HIP runtime it was built with, and the
+        # library then binds to that same runtime (the two share a soname;
+        # whichever loads first serves the process)
+        import torch  # noqa: F401
+
         L = C.CDLL(LIB_PATH)
         vp = C.c_void_p
         L.ep_status_string.argtypes = [C.c_int]

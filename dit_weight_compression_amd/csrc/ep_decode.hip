@@ -62,8 +62,9 @@ constexpr size_t kMaxLds = 160 * 1024;
 //   packed wide (LDS, b = 10, 11, alphabets <= 1024, f < 2^11):
 //             (slot - cum) | f << 11 | symbol << 22.
 //   narrow    (LDS, b = 12, alphabets <= 256): u8 slot -> symbol maps, then per
-//             symbol u32 f | (cum + coset*2^b) << 16 (bit 15: parity of z) and
-//             the float value 2 z + c (4 m + c for m), at stride 256.
+//             symbol a pair of words, u32 f | (cum + coset*2^b) << 16 (bit 15:
+//             parity of z) and the float value 2 z + c (4 m + c for m), at a
+//             stride of 256 pairs, so that one 8-byte read gets both.
 //   workspace (anything else): the narrow scheme with u16 slot maps and stride
 //             2^b, read from the workspace through the caches.
 //   hybrid    (b = 11, 12 with alphabets too large for the above): the
@@ -329,8 +330,9 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   const bool bywrite = (T.byte_cand == 1u && field <= 7) || by16;
   uint32_t* lutb = reinterpret_cast<uint32_t*>(T.tab + byte_off_of(b)) + (size_t(t) << b);
   const size_t lb = lut_bytes_of(tl, b);
-  uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S;
-  float* val = reinterpret_cast<float*>(T.tab + lb + size_t(16) * S * 4) + size_t(t) * S;
+  // per-symbol pairs (entry, value) of the narrow, workspace and hybrid layouts
+  uint32_t* sym = reinterpret_cast<uint32_t*>(T.tab + lb) + size_t(t) * S * 2u;
+  float* val = reinterpret_cast<float*>(sym) + 1;
   extern __shared__ __align__(16) uint32_t build_lds[];
   uint32_t* st32 = build_lds;                  // packed layouts: staged entries, packed then byte
   uint32_t* stb = build_lds + M;
@@ -340,8 +342,8 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
   __shared__ uint32_t part[4];
   if (!is_packed(tl)) {
     for (uint32_t i = A + threadIdx.x; i < S; i += blockDim.x) {
-      sym[i] = 0;
-      val[i] = 0.0f;
+      sym[2u * i] = 0;
+      val[2u * i] = 0.0f;
     }
   }
   if (A == 0) {   // empty table: never used, the decoder flags the tile
@@ -376,9 +378,9 @@ __global__ __launch_bounds__(256) void build_tables_kernel(DevTensor* __restrict
       if (!is_packed(tl)) {
         // the narrow layout (b = 12, f <= 4096) keeps the parity of the value z in bit 15
         const uint32_t zpar = (tl == kTabNarrow && field < 8) ? (uint32_t(int32_t(i) + mn) & 1u) << 15 : 0u;
-        sym[i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
+        sym[2u * i] = (f & 0xFFFFu) | zpar | ((cum + (c << b)) << 16);
         const int32_t z = int32_t(i) + mn;
-        val[i] = float(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
+        val[2u * i] = float(field < 8 || T.f8z8 ? 2 * z + int32_t(c) : 4 * z + int32_t(c));
       }
       cum += f;
     }
@@ -1000,7 +1002,7 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
         lb[c] = cs[c] ? M : 0u;                            // coset offset inside each table pair
         // symbol tables: coset base including the block's own offset, so that
         // the per-field LDS offsets fit the 16-bit immediate
-        cb[c] = cs[c] ? lut_bytes + S * 4u : lut_bytes;
+        cb[c] = cs[c] ? lut_bytes + S * 8u : lut_bytes;
         if (TL == kTabNarrow) asm volatile("" : "+v"(cb[c]));
       }
 #pragma unroll
@@ -1013,9 +1015,11 @@ __device__ __forceinline__ void decode_tiles(const DevTensor& T, uint32_t tile0,
           if (kWs) s = reinterpret_cast<const uint16_t*>(tbase)[(uint32_t(2 * (f - 1)) << B) + addr[c]];
           else if (kHyb) s = reinterpret_cast<const uint16_t*>(lds)[(uint32_t(2 * (f - 1)) << B) + addr[c]];
           else s = lds[(uint32_t(2 * (f - 1)) << B) + addr[c]];
-          const uint32_t eo = cb[c] + s * 4u + uint32_t(f - 1) * 2u * S * 4u;
-          e[c] = *reinterpret_cast<const uint32_t*>(tbase + eo);
-          vv[c][f] = *reinterpret_cast<const float*>(tbase + eo + 16u * S * 4u);
+          // the symbol's entry and value in one 8-byte read
+          const uint32_t eo = cb[c] + s * 8u + uint32_t(f - 1) * 2u * S * 8u;
+          const uint64_t ev2 = *reinterpret_cast<const uint64_t*>(tbase + eo);
+          e[c] = uint32_t(ev2);
+          vv[c][f] = __uint_as_float(uint32_t(ev2 >> 32));
           sv[c][f] = kGlobalEntries ? s : e[c];
         }
 #pragma unroll
