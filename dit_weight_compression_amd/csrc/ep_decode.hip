@@ -1175,9 +1175,16 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DevTensor* __restr
   constexpr uint32_t kGroup = 2u * CH;                     // tiles per wave group
   __shared__ __align__(16) unsigned char smem[kTab + ring_bytes_of(CH)];
   // an even share of the chunks per block (chunks are one group of tiles, so
-  // the blocks' shares differ by at most one group)
-  const uint32_t c0 = uint32_t((uint64_t(blockIdx.x) * nchunks) / gridDim.x);
-  const uint32_t c1 = uint32_t((uint64_t(blockIdx.x + 1u) * nchunks) / gridDim.x);
+  // the blocks' shares differ by at most one group).  Blocks go to the eight
+  // XCDs in turn (block b to XCD b mod 8), each with its own L2: the blocks of
+  // one XCD take consecutive shares, so that a tensor's tables and the cache
+  // lines that neighbouring tiles share are fetched into one L2 rather than
+  // into the L2s of every XCD that holds a neighbouring block.
+  constexpr uint32_t kXcds = 8;
+  const uint32_t nb = gridDim.x, xcd = blockIdx.x % kXcds;
+  const uint32_t lblock = xcd * (nb / kXcds) + min(xcd, nb % kXcds) + blockIdx.x / kXcds;
+  const uint32_t c0 = uint32_t((uint64_t(lblock) * nchunks) / nb);
+  const uint32_t c1 = uint32_t((uint64_t(lblock + 1u) * nchunks) / nb);
   const bool lane0 = (threadIdx.x & 63u) == 0;
   // LDS: [decode tables (LDS layouts)][2 * CH rings of kRingWords per wave]
   uint16_t* rings = reinterpret_cast<uint16_t*>(smem + kTab) + (threadIdx.x >> 6) * (kGroup * kRingWords);
