@@ -1426,13 +1426,30 @@ int make_layout(const ep_tensor_desc* descs, const int* dtypes, int n, Layout& L
   L.group.resize(n);
   L.byte_cand.resize(n);
   for (uint32_t v = 0; v < kNumGroups; ++v) L.group_tiles[v] = 0;
+  bool has_wide[2] = {false, false};               // a tensor of the batch needs the wide layout at b = 10, 11
   for (int i = 0; i < n; ++i) {
     int rc = validate(descs[i], i);
     if (rc != EP_OK) return rc;
+    L.variant[i] = choose_variant(descs[i]);
+    if (L.variant[i] == kVarW10 || L.variant[i] == kVarW11) has_wide[L.variant[i] - kVarW10] = true;
+  }
+  // Each layout is a launch of its own, and a launch ends with a partial last
+  // round.  Where a batch holds wide tensors, its packed tensors of the same b
+  // that the wide entries can hold (no one-symbol table at b = 11) join the wide
+  // launch: one launch and one tail instead of two.  The choice depends on the
+  // descriptors only, so the workspace size is the same with and without dtypes.
+  for (int i = 0; i < n; ++i) {
+    const ep_tensor_desc& d = descs[i];
+    if ((L.variant[i] == kVarP10 || L.variant[i] == kVarP11) && has_wide[L.variant[i] - kVarP10]) {
+      bool single = false;
+      for (int k = 1; k < kTables; ++k) single |= d.alphabet[k] == 1;
+      if (!(d.prob_bits == 11 && single)) L.variant[i] = kVarW10 + (L.variant[i] - kVarP10);
+    }
+  }
+  for (int i = 0; i < n; ++i) {
     const ep_tensor_desc& d = descs[i];
     const int ok = dtypes ? out_kind_of(dtypes[i]) : kOutBF16;
     if (ok < 0) return fail(EP_ERR_INVALID_ARG, "tensor " + std::to_string(i) + ": unknown output dtype");
-    L.variant[i] = choose_variant(d);
     L.group[i] = L.variant[i] * kNumOutKinds + uint32_t(ok);
     L.tab_bytes[i] = storage_bytes_of(layout_of(L.variant[i]), d.prob_bits);
     L.byte_cand[i] = char(byte_mode(d, L.variant[i]));

@@ -154,3 +154,38 @@ def test_hybrid_b11_falls_back_when_values_leave_16_bits(coding):
     assert _max_f(base, range(1, 17)) < 128
     ct = _shift(base, 3, 17000)
     _run(ct, {"variant": H11, "split": 0}, f"hybrid b=11 i16 fallback, {coding}")
+
+
+def _read_batch_variants(cts):
+    ps = [ep.PackedTensor.from_arrays(ct, device="cuda") for ct in cts]
+    outs = ep.alloc_outputs(ps, ["bf16"] * len(ps), "cuda")
+    ws = torch.empty(ep.workspace_size(ps), dtype=torch.uint8, device="cuda")
+    batch = ep.BatchArgs(ps, ["bf16"] * len(ps), outs, None, ws)
+    batch.prepare(ep.C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    rec = ws[: DEVTENSOR_BYTES * len(ps)].cpu().numpy().view(np.uint32)
+    return [int(rec[(i * DEVTENSOR_BYTES + FIELD_OFFSET["variant"]) // 4]) for i in range(len(ps))]
+
+
+def test_packed_tensors_join_the_wide_launch_of_their_batch():
+    # a packed-size tensor decodes in the wide layout when its batch has a wide
+    # tensor at the same b (one launch instead of two), except with a one-symbol
+    # table, whose f = 2^11 the wide entries cannot hold; alone it stays packed
+    packed = _encode(256, 4096, 4.3)
+    wide = _encode(512, 4096, 5.0, outliers=0.002)
+    single = oracle.encode(np.zeros((16, 256), np.float32), 4.0, b=11)
+    assert int(packed.alphabet[1:].max()) <= 512 and 512 < int(wide.alphabet[1:].max()) <= 1024
+    assert single.b == 11 and any(single.alphabet[k] == 1 for k in range(1, 17))
+    assert _read_batch_variants([packed]) == [P11]
+    assert _read_batch_variants([packed, wide, single]) == [W11, W11, P11]
+    cts = [packed, wide, single]
+    for kind in ("bf16", "int8", "lattice2x"):
+        outs, sts = ep.decode_batch([ep.PackedTensor.from_arrays(ct, device="cuda") for ct in cts], [kind] * 3,
+                                    with_status=True)
+        torch.cuda.synchronize()
+        for i, ct in enumerate(cts):
+            ref, rst = oracle.decode(ct, kind)
+            out = outs[i]
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16) if kind == "bf16" else out.cpu().numpy()
+            assert np.all(rst == 0) and np.all(sts[i].cpu().numpy()[: ct.T] == 0), f"tensor {i} {kind}: status"
+            assert np.array_equal(got, ref), f"tensor {i} {kind}: {int(np.sum(got != ref))} mismatches"
