@@ -470,17 +470,31 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // order.  Clamping to [-128, 127] first is the same as rounding first (the
 // bounds are integers); adding 2^23 + 2^22 (+ 128) then rounds to nearest
 // even and leaves the two's-complement code (or the offset code) in the low
-// byte of the sum's bit pattern, and byte permutes gather the four low bytes.
+// byte of the sum's bit pattern.  The first sum is a whole word; the other
+// three are sub-dword adds that write their low byte into byte 1, 2, 3 of that
+// word and keep the rest, so the word ends up holding the four codes.
+template <int BYTE>
+__device__ __forceinline__ void add_f32_to_byte(uint32_t& w, float x, float m) {
+  if constexpr (BYTE == 1)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(x), "v"(m));
+  else if constexpr (BYTE == 2)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(x), "v"(m));
+  else
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(w) : "v"(x), "v"(m));
+}
 template <bool kUnsigned>
 __device__ __forceinline__ uint32_t int8_codes4(float a, float b, float c, float d) {
   constexpr float kMagic = kUnsigned ? 12583040.0f : 12582912.0f;
-  const uint32_t ta = __float_as_uint(__builtin_amdgcn_fmed3f(a, -128.0f, 127.0f) + kMagic);
-  const uint32_t tb = __float_as_uint(__builtin_amdgcn_fmed3f(b, -128.0f, 127.0f) + kMagic);
-  const uint32_t tc = __float_as_uint(__builtin_amdgcn_fmed3f(c, -128.0f, 127.0f) + kMagic);
-  const uint32_t td = __float_as_uint(__builtin_amdgcn_fmed3f(d, -128.0f, 127.0f) + kMagic);
-  const uint32_t lo = __builtin_amdgcn_perm(tb, ta, 0x0C0C0400u);   // a.b0, b.b0, 0, 0
-  const uint32_t hi = __builtin_amdgcn_perm(td, tc, 0x0C0C0400u);   // c.b0, d.b0, 0, 0
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  float m = kMagic;
+  asm volatile("" : "+v"(m));                                     // the sub-dword adds take it from a VGPR
+  uint32_t w = __float_as_uint(__builtin_amdgcn_fmed3f(a, -128.0f, 127.0f) + m);
+  add_f32_to_byte<1>(w, __builtin_amdgcn_fmed3f(b, -128.0f, 127.0f), m);
+  add_f32_to_byte<2>(w, __builtin_amdgcn_fmed3f(c, -128.0f, 127.0f), m);
+  add_f32_to_byte<3>(w, __builtin_amdgcn_fmed3f(d, -128.0f, 127.0f), m);
+  return w;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
